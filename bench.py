@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the BF16 x NVFP4 GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 50]
+
+A step is one decode pass of the GEMM hot path over the four linear layers of
+a Llama-3-70B block at m = 16 (fused QKV 10240x8192, O 8192x8192, fused
+gate/up 57344x8192, down 8192x28672; NVFP4 weights, synthetic seeded inputs of
+the Petit blog's GEMM workload, section "Detailed performance analysis").
+Protocol from the same section: 50 warm-up runs, mean over 100 timed runs.
+Every launch reads a different copy of its layer's packed weights (copies per
+layer >= 1 GiB in total) so the 256 MB last-level cache cannot serve them.
+
+Printed as the last stdout line, one JSON object:
+  value        aggregate algorithmic HBM GB/s of the decode step
+               (bytes = N*K/2 codes + N*K/16 scales + 2*m*K + 2*m*N per GEMM)
+  roofline     the gate/up GEMM (largest share of the step): algorithmic bytes
+               per launch / mean launch time from HIP events around each of
+               its launches on the launch stream, against 8 TB/s
+  prefill      the same four layers at m = 256: TFLOP/s against the 2.5
+               PFLOP/s dense BF16 matrix-core peak
+  cpu_baseline the CPU oracle (float64 NumPy) timed on a bounded sample
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix-core peak
+METRIC = "BF16×NVFP4 GEMM: HBM GB/s at m=16, TFLOP/s at m=256, % of roofline"
+ROTATE_BYTES = 1 << 30
+
+
+def algorithmic_bytes(m, N, K, G):
+    return N * K // 2 + N * K // G + 2 * m * K + 2 * m * N
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--prefill-launches", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """Packed weights of one layer, rotated over R device copies."""
+
+    def __init__(self, prob, F, torch):
+        self.name, self.N, self.K, self.fmt, self.G = prob.name.split("_m")[0], prob.N, prob.K, prob.fmt, prob.group
+        wq, sq = F.repack(prob.codes, prob.scales, prob.N, prob.K, prob.fmt)
+        wq_d, sq_d = F.upload(wq, sq)
+        self.R = max(1, math.ceil(ROTATE_BYTES / (wq.size + sq.size)))
+        self.wq = [wq_d] + [wq_d.clone() for _ in range(self.R - 1)]
+        self.sq = [sq_d] + [sq_d.clone() for _ in range(self.R - 1)]
+
+
+def make_call(F, torch, layer, A, C, r):
+    """Pre-marshalled fp4_gemm call on torch's current stream."""
+    lib = F.lib()
+    stream = F._c_vp(torch.cuda.current_stream().cuda_stream)
+    m = A.shape[0]
+    args = (F._dev_ptr(A), F._dev_ptr(layer.wq[r]), F._dev_ptr(layer.sq[r]), F._dev_ptr(C), m, layer.N, layer.K,
+            layer.fmt, None, 0, stream)
+    fn = lib.fp4_gemm
+
+    def call():
+        st = fn(*args)
+        if st:
+            F._check(st, "fp4_gemm")
+    return call
+
+
+def cpu_baseline(decode_layers_probs):
+    """The oracle as it stands (float64 NumPy: dequant + library matmul) on a
+    bounded sample: m = 16 against the first 8192 rows of the gate/up weights."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    p = decode_layers_probs[2]
+    rows = 8192
+    codes, scales = p.codes[:rows], p.scales[:rows]
+    reps, times = 0, []
+    t_end = time.perf_counter() + 12.0
+    while reps < 3 and (reps == 0 or time.perf_counter() < t_end):
+        t0 = time.perf_counter()
+        oracle.gemm_reference(p.a_bits, codes, scales, p.K, p.fmt)
+        times.append(time.perf_counter() - t0)
+        reps += 1
+    t = float(np.mean(times))
+    b = algorithmic_bytes(p.m, rows, p.K, p.group)
+    return {"value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"m=16 x first {rows} rows of the gate_up weights (K={p.K}), float64 NumPy dequant + "
+                      f"matmul, mean of {reps} runs ({t:.2f} s each); elementwise dequant runs on one thread, "
+                      f"the matmul on {blas_threads} BLAS threads",
+            "seconds_per_run": round(t, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this GEMM has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mixed_precision_bf16_amd import fp4gemm as F
+    from mixed_precision_bf16_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    F.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    t0 = time.time()
+    probs = [synth.make_problem(1, si, 0) for si in range(4)]
+    layers = [Layer(p, F, torch) for p in probs]
+    log(f"inputs ready in {time.time() - t0:.1f}s; rotation copies {[l.R for l in layers]}")
+    m = 16
+    A = [torch.from_numpy(p.a_bits.view(np.int16)).to(dev).view(torch.bfloat16) for p in probs]
+    C = [torch.empty((m, l.N), dtype=torch.bfloat16, device=dev) for l in layers]
+    calls = [[make_call(F, torch, l, A[i], C[i], r) for r in range(l.R)] for i, l in enumerate(layers)]
+    bytes_step = sum(algorithmic_bytes(m, l.N, l.K, l.G) for l in layers)
+    dom = 2  # gate_up
+
+    def step(s, ev=None):
+        for i, l in enumerate(layers):
+            if ev is not None and i == dom:
+                ev[0].record()
+                calls[i][s % l.R]()
+                ev[1].record()
+            else:
+                calls[i][s % l.R]()
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev_dom = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(args.warmup + s, ev_dom[s])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    dom_us = float(np.mean([a.elapsed_time(b) for a, b in ev_dom])) * 1e3
+    gbs = bytes_step / (ms_step * 1e-3) / 1e9
+    dl = layers[dom]
+    dom_bytes = algorithmic_bytes(m, dl.N, dl.K, dl.G)
+    dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
+    log(f"decode step {ms_step * 1e3:.1f} us -> {gbs:.0f} GB/s; gate_up launch {dom_us:.1f} us -> {dom_gbs:.0f} GB/s")
+
+    # per-layer launch times (outside the timed step loop; each layer alone)
+    per_layer = {}
+    for i, l in enumerate(layers):
+        n = 2 * l.R
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(n):
+            calls[i][s % l.R]()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / n * 1e3
+        b = algorithmic_bytes(m, l.N, l.K, l.G)
+        per_layer[l.name] = {"N": l.N, "K": l.K, "us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
+                             "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+    prefill = None
+    if not args.no_prefill:
+        mp = 256
+        rng = np.random.Generator(np.random.PCG64(2_000_000))
+        pre = {}
+        tot_f, tot_t = 0.0, 0.0
+        for i, l in enumerate(layers):
+            a = torch.from_numpy(rng.standard_normal((mp, l.K), dtype=np.float32)).to(torch.bfloat16).to(dev)
+            c = torch.empty((mp, l.N), dtype=torch.bfloat16, device=dev)
+            pc = [make_call(F, torch, l, a, c, r) for r in range(l.R)]
+            for s in range(5):
+                pc[s % l.R]()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = args.prefill_launches
+            e0.record()
+            for s in range(n):
+                pc[s % l.R]()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / n * 1e3
+            fl = 2.0 * mp * l.N * l.K
+            tot_f += fl
+            tot_t += us
+            pre[l.name] = {"us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
+                           "frac_mfma": round(fl / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        prefill = {"m": mp, "layers": pre, "TFLOP/s": round(tot_f / tot_t / 1e6, 1),
+                   "frac_mfma": round(tot_f / tot_t / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS,
+                   "note": "weights of the decode layers; A drawn N(0,1) in BF16 with its own seed"}
+        log(f"prefill m=256: {prefill['TFLOP/s']} TFLOP/s")
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(probs)
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode NVFP4 GEMM, m=16, Llama-3-70B layer shapes "
+                               "(qkv 10240x8192, o 8192x8192, gate_up 57344x8192, down 8192x28672)",
+                   "m": m, "weights": "nvfp4 (E2M1 codes, E4M3 scale per 16)", "activations": "bf16",
+                   "accumulate": "fp32", "rotating_weight_copies": {l.name: l.R for l in layers}},
+        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"kernel": "gemm_skinny (gate_up, m=16)", "bound": "hbm", "achieved": round(dom_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_us, 2), "traffic": None},
+        "layers": per_layer,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * fp4gemm.h -- C ABI of the BF16 x FP4 block-scaled GEMM for AMD MI355X (gfx950).
+ *
+ *   Y[m][N] = A[m][K] . dequant(W)[N][K]^T,   dequant(W)[n][k] = e2m1(code[n][k]) * scale[n][k / G]
+ *
+ * A and Y are BF16, accumulation is FP32.  W is stored as FP4 E2M1 codes with
+ * one scale per G consecutive K-elements of a row:
+ *   NVFP4: G = 16, scale = FP8 E4M3 (OCP "E4M3FN")  -- Petit blog ("Optimizing
+ *          FP4 Mixed-Precision Inference on AMD GPUs"), section "Detailed
+ *          performance analysis": 16 elements share one FP8 scale.
+ *   MXFP4: G = 32, scale = E8M0 (2^(byte - 127))     -- petit-kernel PyPI page,
+ *          "Features": dense GEMM with MXFP4 weights (OCP MX definition).
+ * E2M1 (1 sign, 2 exponent, 1 mantissa bit; values +-{0, .5, 1, 1.5, 2, 3, 4, 6})
+ * follows the mhpq.cn FP4 GEMM article, section 2.1.
+ *
+ * Canonical (source) weight layout, as produced by a quantizer:
+ *   codes  uint8 [N][K/2]  byte j of row n: element k = 2j in bits 3..0,
+ *                          element k = 2j+1 in bits 7..4
+ *   scales uint8 [N][K/G]  byte g of row n scales elements [g*G, (g+1)*G)
+ * The GEMM consumes the "packed" layout written by fp4_repack: the same bytes
+ * permuted into the order in which the gfx950 matrix-core fragments consume
+ * them, so that each wavefront load is one contiguous 1 KiB block (the
+ * offline weight shuffle of the Petit blog, section "Efficient dequantization
+ * through preprocessing", and of the petit-kernel page, "Techniques and
+ * performance").  The packed layout pads N to a multiple of 16 and K to a
+ * multiple of 512 with zero bytes; it is an internal format, described in
+ * the library sources, and may change between versions: persist the
+ * canonical layout (fp4_unpack restores it exactly).
+ *
+ * Conventions for every call:
+ *   - All sizes are element counts unless named *_bytes.  Return value is an
+ *     fp4_status; no call aborts, throws or prints.
+ *   - Every argument check happens before any HIP call.  A failed check
+ *     leaves every output untouched.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronizes inside fp4_gemm / fp4_dequant.
+ *   - "device" pointers must be HIP device memory on the current device;
+ *     "host" pointers must be ordinary host memory.
+ *   - Functions are reentrant and thread-safe; the only global state is a
+ *     per-device "is gfx950" cache.
+ */
+#ifndef FP4GEMM_H
+#define FP4GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats. */
+enum {
+    FP4_NVFP4 = 0, /* G = 16, E4M3 scales */
+    FP4_MXFP4 = 1  /* G = 32, E8M0 scales */
+};
+
+/* Status codes. */
+enum {
+    FP4_OK = 0,
+    FP4_ERR_NULL = 1,      /* a required pointer is NULL */
+    FP4_ERR_SHAPE = 2,     /* N < 1, K < G, K % G != 0, m < 0, or a size over the limits below */
+    FP4_ERR_FORMAT = 3,    /* format is neither FP4_NVFP4 nor FP4_MXFP4 */
+    FP4_ERR_VALUE = 4,     /* fp4_repack: a scale byte is negative or NaN */
+    FP4_ERR_WORKSPACE = 5, /* workspace smaller than fp4_gemm_workspace_size */
+    FP4_ERR_DEVICE = 6,    /* no current HIP device, or it is not gfx950 */
+    FP4_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed */
+};
+
+/* Size limits (checked; FP4_ERR_SHAPE beyond them):
+ *   K <= 2^20, N <= 2^24, m <= 2^20, and m*K*2 and m*N*2 (bytes of A and Y,
+ *   after m is rounded up to the kernel's row block) below 2^31, because the
+ *   kernels address A and Y through 32-bit ranged buffer offsets. */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fp4_status_string(int status);
+
+/* Bytes of the packed code and scale arrays for an N x K weight.
+ * wq_bytes = Np*Kp/2 and sq_bytes = Np*Kp/G with Np = roundup(N, 16),
+ * Kp = roundup(K, 512).  Either output pointer may be NULL. */
+int fp4_repack_size(int64_t N, int64_t K, int format, size_t* wq_bytes, size_t* sq_bytes);
+
+/* Offline, host to host: permute canonical codes [N][K/2] and scales [N][K/G]
+ * into the packed layout wq / sq (sizes from fp4_repack_size; every byte of
+ * both outputs is written, padding with zeros).  Pure integer permutation:
+ * no value changes.  Scale bytes must be non-negative and not NaN (the
+ * petit-kernel page, "Known limitations", assumes positive scales):
+ * NVFP4 rejects bytes with bit 7 set and 0x7F; MXFP4 rejects 0xFF; zero
+ * scales are accepted.  All 16 code values are accepted (a negative-zero code
+ * dequantizes to -0.0).  On FP4_ERR_VALUE nothing is written.
+ * MXFP4 scale bytes outside 2..252 (exponent outside -125..125) are accepted
+ * but give BF16 results that overflow or fall below the normal range. */
+int fp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, int format,
+               uint8_t* wq, uint8_t* sq);
+
+/* Exact inverse of fp4_repack (host to host): writes codes [N][K/2] and
+ * scales [N][K/G].  unpack(repack(x)) == x byte for byte. */
+int fp4_unpack(const uint8_t* wq, const uint8_t* sq, int64_t N, int64_t K, int format,
+               uint8_t* codes, uint8_t* scales);
+
+/* Workspace bytes fp4_gemm needs for this problem (0 when none). */
+int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int format, size_t* bytes);
+
+/* Y = A . dequant(W)^T on `stream` (a hipStream_t; NULL = default stream).
+ *   A   device, BF16 [m][K] row-major, contiguous
+ *   wq  device, packed codes from fp4_repack (uploaded by the caller)
+ *   sq  device, packed scales from fp4_repack
+ *   C   device, BF16 [m][N] row-major, contiguous; every element is written
+ *   workspace / workspace_bytes: device scratch of at least
+ *       fp4_gemm_workspace_size bytes (may be NULL when that size is 0);
+ *       its contents on entry do not matter.  One workspace must not be used
+ *       by two launches that may run at the same time.
+ * m == 0 is a no-op returning FP4_OK.  Asynchronous: returns once the kernels
+ * are queued; faults surface at the caller's next synchronization.
+ * Accumulation is FP32; the output is rounded to BF16 to nearest even. */
+int fp4_gemm(const void* A, const void* wq, const void* sq, void* C,
+             int64_t m, int64_t N, int64_t K, int format,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Debug/test entry: write dequant(W) as BF16 [N][K] row-major to device
+ * memory W_bf16 with the same device dequantization the GEMM uses (the
+ * per-block debug dump suggested by the mhpq.cn article, section 7).
+ * Every code x scale product is exact in BF16 for valid scales. */
+int fp4_dequant(const void* wq, const void* sq, void* W_bf16, int64_t N, int64_t K, int format,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4GEMM_H */

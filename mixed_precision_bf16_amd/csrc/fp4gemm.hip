@@ -1,0 +1,471 @@
+// BF16 x FP4 (NVFP4 / MXFP4) GEMM kernels for gfx950 and the device-side C ABI.
+//
+//   Y[m][N] = A[m][K] . dequant(W)[N][K]^T, FP32 accumulation, BF16 output.
+//
+// Design (MI355X-first; the Petit blog "Optimizing FP4 Mixed-Precision
+// Inference on AMD GPUs" is prior art written for MI300):
+//  * Weights stay FP4 in HBM and are dequantized in registers to BF16 right
+//    before the BF16 matrix-core instruction (the blog's section "Efficient
+//    dequantization through preprocessing": no native FP4 x BF16 matrix core,
+//    so FP4 -> BF16 in registers, then BF16 MFMA).  Activations are never
+//    re-quantized.
+//  * The weight layout is pre-arranged offline (layout.h) so that each lane
+//    loads its MFMA fragment straight from HBM into VGPRs with one 16-byte
+//    load and a wave reads one contiguous 1 KiB block.
+//  * Activations are read with ranged buffer loads: rows >= m and K-padding
+//    read as zero without branches (the blog's section "Generating
+//    high-quality machine code": ranged buffer loads drop out-of-bounds
+//    accesses).
+//  * The activation tile of the large-m kernel is staged in LDS with an XOR
+//    swizzle so that both the 16-byte writes and the fragment reads are free
+//    of bank conflicts (the blog's section "Mastering the memory hierarchy").
+//  * Dequant: gfx950 v_cvt_scalef32_pk_{f32,bf16}_fp4 converts two E2M1 codes
+//    per instruction.  Its scale operand only contributes its exponent
+//    (checked on the device), which is exactly an E8M0 scale, so MXFP4 is
+//    one instruction per two weights.  E4M3 scales carry mantissa bits, so
+//    NVFP4 converts exactly to FP32, multiplies by the decoded scale (exact:
+//    at most 6 significant bits) and keeps the upper halves (exact BF16).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/fp4gemm.h"
+#include "layout.h"
+
+int fp4_check_weight_shape(int64_t N, int64_t K, int format);  // repack.cpp
+
+namespace fp4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer resource word 3 for raw (stride 0) 32-bit buffer access on gfx9-family
+// parts; an offset at or past the buffer's byte range reads zero.
+constexpr int kBufWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// ------------------------------------------------------------------ dequant
+// Keep the upper 16 bits of two FP32 values (exact when both are BF16 values).
+__device__ __forceinline__ uint32_t upper_halves(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// NVFP4: eight codes (low nibble of byte 0 first) times FP32 scale s -> eight
+// BF16 values in K order, packed two per dword.
+__device__ __forceinline__ u32x4 dequant_nvfp4(uint32_t w, float s) {
+    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    u32x4 o;
+    o.x = upper_halves(f0.x * s, f0.y * s);
+    o.y = upper_halves(f1.x * s, f1.y * s);
+    o.z = upper_halves(f2.x * s, f2.y * s);
+    o.w = upper_halves(f3.x * s, f3.y * s);
+    return o;
+}
+
+// MXFP4: the scale operand is an FP32 whose exponent field is the E8M0 byte.
+__device__ __forceinline__ u32x4 dequant_mxfp4(uint32_t w, float sexp) {
+    u32x4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sexp, 0));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sexp, 1));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sexp, 2));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sexp, 3));
+    return o;
+}
+
+// Scale words of one lane for one 512-K scale block (layout.h).
+template <int FMT> struct ScaleWord;
+template <> struct ScaleWord<0> { typedef u32x2 type; };
+template <> struct ScaleWord<1> { typedef uint32_t type; };
+
+// Scale operand for chunk C (0..3) of the block and half H (0: dwords 0-1,
+// 1: dwords 2-3 of the lane's 32 K).  NVFP4: OCP E4M3 -> FP32 via the
+// hardware FP8 convert (OCP encoding on gfx950, checked on the device).
+template <int C, int H>
+__device__ __forceinline__ float nv_scale(u32x2 s) {
+    constexpr int byte = 2 * C + H;
+    const uint32_t word = (byte < 4) ? s.x : s.y;
+    return __builtin_amdgcn_cvt_f32_fp8((int)word, byte & 3);
+}
+template <int C>
+__device__ __forceinline__ float mx_scale(uint32_t s) {
+    return __uint_as_float(((s >> (8 * C)) & 0xFFu) << 23);
+}
+
+// Dequantize MFMA step I (dword I of the lane's 16 bytes) of chunk C.
+template <int FMT, int C, int I>
+__device__ __forceinline__ u32x4 dequant_step(const u32x4& w, const typename ScaleWord<FMT>::type& s) {
+    if constexpr (FMT == 0) {
+        return dequant_nvfp4(w[I], nv_scale<C, I / 2>(s));
+    } else {
+        return dequant_mxfp4(w[I], mx_scale<C>(s));
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ typename ScaleWord<FMT>::type load_scales(const uint8_t* __restrict__ sq, size_t blk,
+                                                                     int lane) {
+    if constexpr (FMT == 0) {
+        return reinterpret_cast<const u32x2*>(sq)[blk * kLanes + lane];
+    } else {
+        return reinterpret_cast<const uint32_t*>(sq)[blk * kLanes + lane];
+    }
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load_a(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Store one 16x16 output fragment: lane holds Y[m][n0 .. n0+3] (MFMA output
+// rows are n, columns are m).
+__device__ __forceinline__ void store_frag(uint16_t* __restrict__ C, const f32x4& v, int m, int n0, int M, int N) {
+    if (m >= M) return;
+    const uint32_t p0 = pack_bf16_rne(v.x, v.y), p1 = pack_bf16_rne(v.z, v.w);
+    uint16_t* dst = C + (size_t)m * N + n0;
+    if ((N & 3) == 0 && n0 + 3 < N) {
+        u32x2 pv = {p0, p1};
+        *reinterpret_cast<u32x2*>(dst) = pv;
+    } else {
+        const uint16_t h[4] = {(uint16_t)(p0 & 0xFFFF), (uint16_t)(p0 >> 16), (uint16_t)(p1 & 0xFFFF),
+                               (uint16_t)(p1 >> 16)};
+        for (int e = 0; e < 4; ++e)
+            if (n0 + e < N) dst[e] = h[e];
+    }
+}
+
+// ------------------------------------------------------------ skinny GEMM
+// Small m (<= 16*MB): each workgroup owns TN n-tiles (16 rows each) and its NW
+// waves split K; every wave streams its share of the tiles' 1 KiB code blocks
+// straight into VGPRs, reads the matching activation fragments (64
+// contiguous bytes per lane per chunk) with ranged buffer loads, and the
+// partial 16x16 products are summed across the waves through LDS in a fixed
+// order (deterministic).
+template <int FMT, int MB, int TN, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny(const uint16_t* __restrict__ A, const u32x4* __restrict__ wq,
+                                                      const uint8_t* __restrict__ sq, uint16_t* __restrict__ C,
+                                                      int M, int N, int K, int KB, int SB, int NT) {
+    typedef typename ScaleWord<FMT>::type SW;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane & 15, j = lane >> 4;
+    const int tile0 = blockIdx.x * TN;
+
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, M * K * 2, kBufWord3);
+    uint32_t arow[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) arow[mb] = (uint32_t)((mb * 16 + r) * K) * 2u;
+
+    int tl[TN];  // tiles past the end re-read the last tile; their stores are masked by n < N
+#pragma unroll
+    for (int tt = 0; tt < TN; ++tt) tl[tt] = min(tile0 + tt, NT - 1);
+
+    f32x4 acc[TN][MB];
+#pragma unroll
+    for (int tt = 0; tt < TN; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int sb0 = (wave * SB) / NW, sb1 = ((wave + 1) * SB) / NW;
+    for (int sb = sb0; sb < sb1; ++sb) {
+        SW sc[TN];
+#pragma unroll
+        for (int tt = 0; tt < TN; ++tt) sc[tt] = load_scales<FMT>(sq, (size_t)tl[tt] * SB + sb, lane);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int b = sb * 4 + c;
+            u32x4 w[TN];
+#pragma unroll
+            for (int tt = 0; tt < TN; ++tt) w[tt] = wq[((size_t)tl[tt] * KB + b) * kLanes + lane];
+            const int kb = b * kChunkK + j * 32;
+            u32x4 a[MB][4];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int k = kb + 8 * i;
+                    a[mb][i] = load_a(ra, k < K ? arow[mb] + (uint32_t)k * 2u : kOutOfRange);
+                }
+#pragma unroll
+            for (int tt = 0; tt < TN; ++tt) {
+                u32x4 wf[4];
+                switch (c) {  // c is a compile-time constant after unrolling
+                    case 0: wf[0] = dequant_step<FMT, 0, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 0, 1>(w[tt], sc[tt]);
+                            wf[2] = dequant_step<FMT, 0, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 0, 3>(w[tt], sc[tt]); break;
+                    case 1: wf[0] = dequant_step<FMT, 1, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 1, 1>(w[tt], sc[tt]);
+                            wf[2] = dequant_step<FMT, 1, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 1, 3>(w[tt], sc[tt]); break;
+                    case 2: wf[0] = dequant_step<FMT, 2, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 2, 1>(w[tt], sc[tt]);
+                            wf[2] = dequant_step<FMT, 2, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 2, 3>(w[tt], sc[tt]); break;
+                    default: wf[0] = dequant_step<FMT, 3, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 3, 1>(w[tt], sc[tt]);
+                             wf[2] = dequant_step<FMT, 3, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 3, 3>(w[tt], sc[tt]); break;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = mfma_bf16(wf[i], a[mb][i], acc[tt][mb]);
+            }
+        }
+    }
+
+    if constexpr (NW > 1) {
+        __shared__ f32x4 red[(NW - 1) * TN * MB * kLanes];
+        if (wave > 0) {
+#pragma unroll
+            for (int tt = 0; tt < TN; ++tt)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) red[(((wave - 1) * TN + tt) * MB + mb) * kLanes + lane] = acc[tt][mb];
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        for (int w = 1; w < NW; ++w)
+#pragma unroll
+            for (int tt = 0; tt < TN; ++tt)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) acc[tt][mb] += red[(((w - 1) * TN + tt) * MB + mb) * kLanes + lane];
+    }
+#pragma unroll
+    for (int tt = 0; tt < TN; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) store_frag(C, acc[tt][mb], mb * 16 + r, (tile0 + tt) * kTileN + 4 * j, M, N);
+}
+
+// ------------------------------------------------------------- tiled GEMM
+// Larger m: a 256-thread workgroup computes a 128 (m) x 128 (n) tile; its four
+// waves form a 2 x 2 grid of 64 x 64 sub-tiles (4 x 4 MFMA fragments each).
+// Per 128-K chunk the activation tile (128 x 128 BF16, 32 KiB) is staged in
+// LDS with an XOR swizzle of its 16-byte columns by row, and each wave loads
+// the 1 KiB code blocks of its four n-tiles directly into VGPRs.
+constexpr int kTiledBM = 128, kTiledBNT = 8;  // m rows, n-tiles per workgroup
+
+template <int FMT>
+__global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A, const u32x4* __restrict__ wq,
+                                                 const uint8_t* __restrict__ sq, uint16_t* __restrict__ C, int M,
+                                                 int N, int K, int KB, int SB, int NT) {
+    typedef typename ScaleWord<FMT>::type SW;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTiledBM * 256];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, j = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int m0 = blockIdx.y * kTiledBM;
+    const int tile0 = blockIdx.x * kTiledBNT + wn * 4;
+
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, M * K * 2, kBufWord3);
+    int tl[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) tl[tt] = min(tile0 + tt, NT - 1);
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int sb = 0; sb < SB; ++sb) {
+        SW sc[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) sc[tt] = load_scales<FMT>(sq, (size_t)tl[tt] * SB + sb, lane);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int b = sb * 4 + c;
+            // stage A[m0 .. m0+127][128 b .. 128 b + 127] into LDS
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int p = tid + 256 * q;
+                const int row = p >> 4, col = p & 15;
+                const int k = b * kChunkK + col * 8;
+                const uint32_t off = k < K ? (uint32_t)((m0 + row) * K + k) * 2u : kOutOfRange;
+                const u32x4 v = load_a(ra, off);
+                *reinterpret_cast<u32x4*>(lds_a + row * 256 + ((col ^ (row & 15)) << 4)) = v;
+            }
+            u32x4 w[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) w[tt] = wq[((size_t)tl[tt] * KB + b) * kLanes + lane];
+            __syncthreads();
+            u32x4 a[4][4];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int row = wm * 64 + mb * 16 + r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int col = j * 4 + i;
+                    a[mb][i] = *reinterpret_cast<const u32x4*>(lds_a + row * 256 + ((col ^ (row & 15)) << 4));
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                u32x4 wf[4];
+                switch (c) {
+                    case 0: wf[0] = dequant_step<FMT, 0, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 0, 1>(w[tt], sc[tt]);
+                            wf[2] = dequant_step<FMT, 0, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 0, 3>(w[tt], sc[tt]); break;
+                    case 1: wf[0] = dequant_step<FMT, 1, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 1, 1>(w[tt], sc[tt]);
+                            wf[2] = dequant_step<FMT, 1, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 1, 3>(w[tt], sc[tt]); break;
+                    case 2: wf[0] = dequant_step<FMT, 2, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 2, 1>(w[tt], sc[tt]);
+                            wf[2] = dequant_step<FMT, 2, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 2, 3>(w[tt], sc[tt]); break;
+                    default: wf[0] = dequant_step<FMT, 3, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 3, 1>(w[tt], sc[tt]);
+                             wf[2] = dequant_step<FMT, 3, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 3, 3>(w[tt], sc[tt]); break;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb) acc[tt][mb] = mfma_bf16(wf[i], a[mb][i], acc[tt][mb]);
+            }
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+            store_frag(C, acc[tt][mb], m0 + wm * 64 + mb * 16 + r, (tile0 + tt) * kTileN + 4 * j, M, N);
+}
+
+// ------------------------------------------------------------ debug dequant
+// One wave per (n-tile, 128-K chunk): writes the BF16 weights it would feed to
+// the matrix core, using the GEMM's own dequant functions.
+template <int FMT>
+__global__ __launch_bounds__(64) void dequant_kernel(const u32x4* __restrict__ wq, const uint8_t* __restrict__ sq,
+                                                     uint16_t* __restrict__ W, int N, int K, int KB, int SB) {
+    typedef typename ScaleWord<FMT>::type SW;
+    const int t = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x, r = lane & 15, j = lane >> 4;
+    const int n = t * kTileN + r;
+    const u32x4 w = wq[((size_t)t * KB + b) * kLanes + lane];
+    const SW s = load_scales<FMT>(sq, (size_t)t * SB + b / 4, lane);
+    u32x4 o[4];
+    switch (b & 3) {
+        case 0: o[0] = dequant_step<FMT, 0, 0>(w, s); o[1] = dequant_step<FMT, 0, 1>(w, s);
+                o[2] = dequant_step<FMT, 0, 2>(w, s); o[3] = dequant_step<FMT, 0, 3>(w, s); break;
+        case 1: o[0] = dequant_step<FMT, 1, 0>(w, s); o[1] = dequant_step<FMT, 1, 1>(w, s);
+                o[2] = dequant_step<FMT, 1, 2>(w, s); o[3] = dequant_step<FMT, 1, 3>(w, s); break;
+        case 2: o[0] = dequant_step<FMT, 2, 0>(w, s); o[1] = dequant_step<FMT, 2, 1>(w, s);
+                o[2] = dequant_step<FMT, 2, 2>(w, s); o[3] = dequant_step<FMT, 2, 3>(w, s); break;
+        default: o[0] = dequant_step<FMT, 3, 0>(w, s); o[1] = dequant_step<FMT, 3, 1>(w, s);
+                 o[2] = dequant_step<FMT, 3, 2>(w, s); o[3] = dequant_step<FMT, 3, 3>(w, s); break;
+    }
+    if (n >= N) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = b * kChunkK + j * 32 + 8 * i;
+        if (k < K) *reinterpret_cast<u32x4*>(W + (size_t)n * K + k) = o[i];
+    }
+}
+
+// ------------------------------------------------------------- host side
+std::atomic<int> g_device_state[64];  // 0 unknown, 1 gfx950, 2 other
+
+static int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FP4_ERR_DEVICE;
+    int st = g_device_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return FP4_ERR_DEVICE;
+        st = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? FP4_OK : FP4_ERR_DEVICE;
+}
+
+static int launch_status() {
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+// Row block the kernel for this m reads A in (A offsets are 32-bit).
+static int64_t a_row_block(int64_t M) {
+    if (M <= 16) return 16;
+    if (M <= 32) return 32;
+    if (M <= 64) return 64;
+    return kTiledBM;
+}
+
+template <int FMT>
+static void launch_gemm(const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, int M, int N, int K,
+                        int KB, int SB, int NT, hipStream_t s) {
+    if (M <= 16) {
+        gemm_skinny<FMT, 1, 1, 4><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+    } else if (M <= 32) {
+        gemm_skinny<FMT, 2, 1, 4><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+    } else if (M <= 64) {
+        gemm_skinny<FMT, 4, 1, 4><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+    } else {
+        dim3 grid((NT + kTiledBNT - 1) / kTiledBNT, (M + kTiledBM - 1) / kTiledBM);
+        gemm_tiled<FMT><<<grid, dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+    }
+}
+
+}  // namespace fp4
+
+using namespace fp4;
+
+extern "C" int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int format, size_t* bytes) {
+    int st = fp4_check_weight_shape(N, K, format);
+    if (st != FP4_OK) return st;
+    if (m < 0 || m > (int64_t(1) << 20)) return FP4_ERR_SHAPE;
+    if (!bytes) return FP4_ERR_NULL;
+    *bytes = 0;
+    return FP4_OK;
+}
+
+extern "C" int fp4_gemm(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
+                        int format, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    int st = fp4_check_weight_shape(N, K, format);
+    if (st != FP4_OK) return st;
+    if (m < 0 || m > (int64_t(1) << 20)) return FP4_ERR_SHAPE;
+    if (m == 0) return FP4_OK;
+    if (!A || !wq || !sq || !C) return FP4_ERR_NULL;
+    if (round_up(m, a_row_block(m)) * K * 2 >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
+    st = check_device();
+    if (st != FP4_OK) return st;
+    const int64_t Np = padded_n(N), Kp = padded_k(K);
+    const int KB = int(Kp / kChunkK), SB = int(Kp / kScaleBlockK), NT = int(Np / kTileN);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (format == FP4_NVFP4)
+        launch_gemm<0>((const uint16_t*)A, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, int(m), int(N), int(K),
+                       KB, SB, NT, s);
+    else
+        launch_gemm<1>((const uint16_t*)A, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, int(m), int(N), int(K),
+                       KB, SB, NT, s);
+    return launch_status();
+}
+
+extern "C" int fp4_dequant(const void* wq, const void* sq, void* W_bf16, int64_t N, int64_t K, int format,
+                           void* stream) {
+    int st = fp4_check_weight_shape(N, K, format);
+    if (st != FP4_OK) return st;
+    if (!wq || !sq || !W_bf16) return FP4_ERR_NULL;
+    st = check_device();
+    if (st != FP4_OK) return st;
+    const int64_t Np = padded_n(N), Kp = padded_k(K);
+    const int KB = int(Kp / kChunkK), SB = int(Kp / kScaleBlockK), NT = int(Np / kTileN);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    dim3 grid(NT, KB);
+    if (format == FP4_NVFP4)
+        dequant_kernel<0><<<grid, dim3(64), 0, s>>>((const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)W_bf16, int(N),
+                                                    int(K), KB, SB);
+    else
+        dequant_kernel<1><<<grid, dim3(64), 0, s>>>((const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)W_bf16, int(N),
+                                                    int(K), KB, SB);
+    return launch_status();
+}

@@ -1,0 +1,99 @@
+// Offline weight repack / unpack and the host-only parts of the C ABI.
+//
+// The repack is the offline weight arrangement of the Petit blog ("Optimizing
+// FP4 Mixed-Precision Inference on AMD GPUs", section "Efficient
+// dequantization through preprocessing") and of the petit-kernel PyPI page
+// ("Techniques and performance": weights are shuffled offline).  Here it is a
+// pure byte permutation (plus zero padding) into the layout of layout.h, so it
+// is exactly invertible and never changes a value.
+#include <string.h>
+
+#include "../../include/fp4gemm.h"
+#include "layout.h"
+
+using namespace fp4;
+
+extern "C" const char* fp4_status_string(int status) {
+    switch (status) {
+        case FP4_OK: return "ok";
+        case FP4_ERR_NULL: return "null pointer argument";
+        case FP4_ERR_SHAPE: return "invalid shape (need N >= 1, K >= G, K % G == 0, m >= 0, within size limits)";
+        case FP4_ERR_FORMAT: return "unknown FP4 format (expected FP4_NVFP4 or FP4_MXFP4)";
+        case FP4_ERR_VALUE: return "invalid scale byte (negative or NaN)";
+        case FP4_ERR_WORKSPACE: return "workspace too small";
+        case FP4_ERR_DEVICE: return "no gfx950 HIP device is current";
+        case FP4_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+// Shared by the host and device entry points (declared in fp4gemm_internal.h).
+int fp4_check_weight_shape(int64_t N, int64_t K, int format) {
+    if (format != FP4_NVFP4 && format != FP4_MXFP4) return FP4_ERR_FORMAT;
+    const int64_t G = group_of(format);
+    if (N < 1 || N > (int64_t(1) << 24)) return FP4_ERR_SHAPE;
+    if (K < G || K % G != 0 || K > (int64_t(1) << 20)) return FP4_ERR_SHAPE;
+    return FP4_OK;
+}
+
+extern "C" int fp4_repack_size(int64_t N, int64_t K, int format, size_t* wq_bytes, size_t* sq_bytes) {
+    int st = fp4_check_weight_shape(N, K, format);
+    if (st != FP4_OK) return st;
+    const int64_t Np = padded_n(N), Kp = padded_k(K);
+    if (wq_bytes) *wq_bytes = size_t(Np * Kp / 2);
+    if (sq_bytes) *sq_bytes = size_t(Np * Kp / group_of(format));
+    return FP4_OK;
+}
+
+static bool scale_byte_ok(uint8_t b, int format) {
+    if (format == FP4_NVFP4) return (b & 0x80) == 0 && b != 0x7F;  // sign clear, not NaN
+    return b != 0xFF;                                              // E8M0 NaN
+}
+
+extern "C" int fp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, int format,
+                          uint8_t* wq, uint8_t* sq) {
+    int st = fp4_check_weight_shape(N, K, format);
+    if (st != FP4_OK) return st;
+    if (!codes || !scales || !wq || !sq) return FP4_ERR_NULL;
+    const int64_t G = group_of(format);
+    const int64_t ng = K / G;
+    for (int64_t i = 0; i < N * ng; ++i)
+        if (!scale_byte_ok(scales[i], format)) return FP4_ERR_VALUE;
+
+    const int64_t Np = padded_n(N), Kp = padded_k(K);
+    const int64_t KB = Kp / kChunkK, SB = Kp / kScaleBlockK;
+    memset(wq, 0, size_t(Np * Kp / 2));
+    memset(sq, 0, size_t(Np * Kp / G));
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t* row = codes + n * (K / 2);
+        // one lane's 16 bytes cover 32 consecutive k of the row
+        for (int64_t k = 0; k < K; k += 32) {
+            const int64_t len = (K - k >= 32) ? 16 : (K - k) / 2;
+            memcpy(wq + wq_offset(n, k, KB), row + k / 2, size_t(len));
+        }
+        const uint8_t* srow = scales + n * ng;
+        for (int64_t g = 0; g < ng; ++g) sq[sq_offset(n, g * G, SB, format)] = srow[g];
+    }
+    return FP4_OK;
+}
+
+extern "C" int fp4_unpack(const uint8_t* wq, const uint8_t* sq, int64_t N, int64_t K, int format,
+                          uint8_t* codes, uint8_t* scales) {
+    int st = fp4_check_weight_shape(N, K, format);
+    if (st != FP4_OK) return st;
+    if (!codes || !scales || !wq || !sq) return FP4_ERR_NULL;
+    const int64_t G = group_of(format);
+    const int64_t ng = K / G;
+    const int64_t Kp = padded_k(K);
+    const int64_t KB = Kp / kChunkK, SB = Kp / kScaleBlockK;
+    for (int64_t n = 0; n < N; ++n) {
+        uint8_t* row = codes + n * (K / 2);
+        for (int64_t k = 0; k < K; k += 32) {
+            const int64_t len = (K - k >= 32) ? 16 : (K - k) / 2;
+            memcpy(row + k / 2, wq + wq_offset(n, k, KB), size_t(len));
+        }
+        uint8_t* srow = scales + n * ng;
+        for (int64_t g = 0; g < ng; ++g) srow[g] = sq[sq_offset(n, g * G, SB, format)];
+    }
+    return FP4_OK;
+}

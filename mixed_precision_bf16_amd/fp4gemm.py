@@ -1,0 +1,185 @@
+"""ctypes binding of ``libfp4gemm.so`` (argument marshalling only).
+
+Every step of the GEMM runs in the HIP library; this module turns NumPy /
+PyTorch buffers into pointers and status codes into exceptions.  PyTorch is
+used for device memory and the current HIP stream.  There is no fallback: if
+the library is missing or the device is not gfx950, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+from . import build as _build
+
+NVFP4 = 0
+MXFP4 = 1
+GROUP = {NVFP4: 16, MXFP4: 32}
+
+_c_i64 = ctypes.c_int64
+_c_vp = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/fp4gemm.h
+_SIGNATURES = {
+    "fp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fp4_repack_size": (ctypes.c_int, [_c_i64, _c_i64, ctypes.c_int, ctypes.POINTER(_c_sz), ctypes.POINTER(_c_sz)]),
+    "fp4_repack": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, _c_vp, _c_vp]),
+    "fp4_unpack": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, _c_vp, _c_vp]),
+    "fp4_gemm_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.POINTER(_c_sz)]),
+    "fp4_gemm": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_vp, _c_sz,
+                                _c_vp]),
+    "fp4_dequant": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
+}
+
+STATUS = {0: "FP4_OK", 1: "FP4_ERR_NULL", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_FORMAT", 4: "FP4_ERR_VALUE",
+          5: "FP4_ERR_WORKSPACE", 6: "FP4_ERR_DEVICE", 7: "FP4_ERR_HIP"}
+
+
+class Fp4Error(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = lib().fp4_status_string(status).decode()
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({msg})")
+
+
+_LIB = None
+
+
+def lib_path() -> str:
+    return _build.LIB_PATH
+
+
+def lib():
+    """Load the library (building it once if it was never built)."""
+    global _LIB
+    if _LIB is None:
+        path = _build.ensure_built()
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def header_functions():
+    """Names of the functions declared in include/fp4gemm.h."""
+    hdr = os.path.join(_build.ROOT, "include", "fp4gemm.h")
+    text = open(hdr).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fp4_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise Fp4Error(status, what)
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(_c_vp)
+
+
+# ------------------------------------------------------------------ host API
+def repack_size(N: int, K: int, fmt: int):
+    wq, sq = _c_sz(), _c_sz()
+    _check(lib().fp4_repack_size(N, K, fmt, ctypes.byref(wq), ctypes.byref(sq)), "fp4_repack_size")
+    return wq.value, sq.value
+
+
+def repack(codes: np.ndarray, scales: np.ndarray, N: int, K: int, fmt: int):
+    """Canonical codes [N][K/2] and scales [N][K/G] (uint8, host) -> packed (wq, sq)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    if codes.size != N * (K // 2) or scales.size != N * (K // GROUP.get(fmt, 1)):
+        raise ValueError("codes / scales do not match N, K, format")
+    nw, ns = repack_size(N, K, fmt)
+    wq = np.empty(nw, dtype=np.uint8)
+    sq = np.empty(ns, dtype=np.uint8)
+    _check(lib().fp4_repack(_np_ptr(codes), _np_ptr(scales), N, K, fmt, _np_ptr(wq), _np_ptr(sq)), "fp4_repack")
+    return wq, sq
+
+
+def unpack(wq: np.ndarray, sq: np.ndarray, N: int, K: int, fmt: int):
+    """Packed (wq, sq) -> canonical (codes [N][K/2], scales [N][K/G])."""
+    nw, ns = repack_size(N, K, fmt)
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    sq = np.ascontiguousarray(sq, dtype=np.uint8)
+    if wq.size != nw or sq.size != ns:
+        raise ValueError("packed arrays have the wrong size")
+    codes = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((N, K // GROUP[fmt]), dtype=np.uint8)
+    _check(lib().fp4_unpack(_np_ptr(wq), _np_ptr(sq), N, K, fmt, _np_ptr(codes), _np_ptr(scales)), "fp4_unpack")
+    return codes, scales
+
+
+def workspace_size(m: int, N: int, K: int, fmt: int) -> int:
+    b = _c_sz()
+    _check(lib().fp4_gemm_workspace_size(m, N, K, fmt, ctypes.byref(b)), "fp4_gemm_workspace_size")
+    return b.value
+
+
+# ---------------------------------------------------------------- device API
+def _dev_ptr(t):
+    return _c_vp(t.data_ptr()) if t is not None else _c_vp(0)
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _c_vp(stream.cuda_stream)
+
+
+def gemm(A, wq, sq, N: int, K: int, fmt: int, out=None, workspace=None, stream=None):
+    """Y = A . dequant(W)^T.  A: bf16 CUDA [m][K]; wq, sq: uint8 CUDA (packed).
+    Returns (or fills) a bf16 CUDA tensor [m][N]."""
+    import torch
+    if A.dtype != torch.bfloat16 or A.dim() != 2 or not A.is_cuda or not A.is_contiguous():
+        raise ValueError("A must be a contiguous 2-D bfloat16 CUDA tensor")
+    if A.shape[1] != K:
+        raise ValueError("A must have K columns")
+    for t in (wq, sq):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("wq / sq must be contiguous uint8 CUDA tensors")
+    nw, ns = repack_size(N, K, fmt)
+    if wq.numel() != nw or sq.numel() != ns:
+        raise ValueError("packed weight tensors have the wrong size")
+    m = A.shape[0]
+    if out is None:
+        out = torch.empty((m, N), dtype=torch.bfloat16, device=A.device)
+    elif out.shape != (m, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor [m][N]")
+    wsb = workspace_size(m, N, K, fmt)
+    if wsb and workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=A.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().fp4_gemm(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), m, N, K, fmt,
+                          _dev_ptr(workspace), ws_bytes, _stream_handle(stream)), "fp4_gemm")
+    return out
+
+
+def dequant(wq, sq, N: int, K: int, fmt: int, out=None, stream=None):
+    """BF16 weights [N][K] exactly as the GEMM feeds them to the matrix core."""
+    import torch
+    nw, ns = repack_size(N, K, fmt)
+    if wq.numel() != nw or sq.numel() != ns or not wq.is_cuda or not sq.is_cuda:
+        raise ValueError("packed weight tensors have the wrong size or device")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=wq.device)
+    _check(lib().fp4_dequant(_dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), N, K, fmt, _stream_handle(stream)),
+           "fp4_dequant")
+    return out
+
+
+def upload(wq: np.ndarray, sq: np.ndarray, device="cuda"):
+    """Copy packed host arrays to device uint8 tensors."""
+    import torch
+    return (torch.from_numpy(np.ascontiguousarray(wq)).to(device),
+            torch.from_numpy(np.ascontiguousarray(sq)).to(device))

@@ -1,0 +1,151 @@
+"""Host-side tests of the C ABI: symbols, offline repack/unpack, argument checks.
+
+No GPU is needed: repack/unpack are pure host functions and every argument
+check of the device entry points runs before any HIP call.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from mixed_precision_bf16_amd import fp4gemm as F
+from mixed_precision_bf16_amd import synth
+
+
+def test_library_exports_every_header_function():
+    lib = F.lib()
+    names = F.header_functions()
+    assert set(names) == set(F._SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(8):
+        assert F.lib().fp4_status_string(s)
+    assert F.lib().fp4_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("N,K,fmt", [(1, 16, 0), (16, 512, 0), (17, 528, 0), (2, 32, 1), (33, 1056, 1),
+                                     (512, 1024, 0), (100, 8192, 1)])
+def test_repack_size(N, K, fmt):
+    G = 16 if fmt == 0 else 32
+    Np = -(-N // 16) * 16
+    Kp = -(-K // 512) * 512
+    assert F.repack_size(N, K, fmt) == (Np * Kp // 2, Np * Kp // G)
+
+
+def _rand_weights(N, K, fmt, seed, all_codes=True):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    G = 16 if fmt == 0 else 32
+    codes = rng.integers(0, 256 if all_codes else 1, size=(N, K // 2), dtype=np.uint8)
+    hi = 0x7F if fmt == 0 else 0xFF
+    scales = rng.integers(0, hi, size=(N, K // G), dtype=np.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("N,K,fmt", [(1, 16, 0), (2, 32, 1), (15, 48, 0), (16, 512, 0), (17, 528, 0),
+                                     (40, 1040, 0), (33, 1056, 1), (130, 2080, 1), (64, 8192, 0)])
+def test_repack_roundtrip_and_padding(N, K, fmt):
+    codes, scales = _rand_weights(N, K, fmt, seed=N * 1000 + K + fmt)
+    wq, sq = F.repack(codes, scales, N, K, fmt)
+    c2, s2 = F.unpack(wq, sq, N, K, fmt)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+    # the packed arrays hold the same multiset of nibbles / scale bytes plus zero padding
+    nib = lambda x: np.bincount(np.concatenate([x.ravel() & 15, x.ravel() >> 4]), minlength=16)
+    pad_nibbles = 2 * wq.size - 2 * codes.size
+    want = nib(codes)
+    want[0] += pad_nibbles
+    assert np.array_equal(nib(wq), want)
+    sb = np.bincount(scales.ravel(), minlength=256)
+    sb[0] += sq.size - scales.size
+    assert np.array_equal(np.bincount(sq, minlength=256), sb)
+
+
+def test_repack_is_a_permutation_of_16_byte_lane_blocks():
+    # Every run of 16 source bytes (32 consecutive k of one row) lands intact
+    # in one 16-byte slot of the packed codes.
+    N, K = 20, 1024
+    codes = np.arange(N * K // 2, dtype=np.uint64).astype(np.uint8).reshape(N, K // 2)
+    codes = ((np.arange(N * K // 2) * 2654435761) >> 7).astype(np.uint8).reshape(N, K // 2)
+    scales = np.full((N, K // 16), 0x38, np.uint8)
+    wq, _ = F.repack(codes, scales, N, K, 0)
+    slots = {bytes(wq[i:i + 16]) for i in range(0, wq.size, 16)}
+    for n in range(N):
+        for k in range(0, K, 32):
+            assert bytes(codes[n, k // 2:k // 2 + 16]) in slots
+
+
+def test_repack_synthetic_config_roundtrip():
+    p = synth.make_problem(0, 0, 0)
+    wq, sq = F.repack(p.codes, p.scales, p.N, p.K, p.fmt)
+    c2, s2 = F.unpack(wq, sq, p.N, p.K, p.fmt)
+    assert np.array_equal(c2, p.codes) and np.array_equal(s2, p.scales)
+
+
+@pytest.mark.parametrize("fmt,bad", [(0, 0x80), (0, 0xB8), (0, 0x7F), (0, 0xFF), (1, 0xFF)])
+def test_repack_rejects_negative_or_nan_scales(fmt, bad):
+    N, K = 4, 64
+    G = 16 if fmt == 0 else 32
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.full((N, K // G), 0x38 if fmt == 0 else 127, np.uint8)
+    scales[2, 1] = bad
+    nw, ns = F.repack_size(N, K, fmt)
+    wq = np.full(nw, 0xAB, np.uint8)
+    sq = np.full(ns, 0xAB, np.uint8)
+    st = F.lib().fp4_repack(F._np_ptr(codes), F._np_ptr(scales), N, K, fmt, F._np_ptr(wq), F._np_ptr(sq))
+    assert st == 4
+    assert np.all(wq == 0xAB) and np.all(sq == 0xAB), "nothing written on error"
+
+
+def test_repack_accepts_zero_scale_and_negative_zero_codes():
+    N, K = 3, 32
+    codes = np.full((N, K // 2), 0x88, np.uint8)
+    scales = np.zeros((N, 2), np.uint8)
+    wq, sq = F.repack(codes, scales, N, K, 0)
+    c2, s2 = F.unpack(wq, sq, N, K, 0)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+
+
+@pytest.mark.parametrize("N,K,fmt,status", [(0, 16, 0, 2), (4, 8, 0, 2), (4, 24, 0, 2), (4, 16, 1, 2),
+                                            (4, 48, 1, 2), (4, 32, 2, 3), (4, 32, -1, 3), (4, 1 << 21, 0, 2)])
+def test_shape_and_format_errors(N, K, fmt, status):
+    sz = ctypes.c_size_t()
+    assert F.lib().fp4_repack_size(N, K, fmt, ctypes.byref(sz), ctypes.byref(sz)) == status
+    assert F.lib().fp4_gemm_workspace_size(16, N, K, fmt, ctypes.byref(sz)) == status
+    dummy = ctypes.c_void_p(1)
+    assert F.lib().fp4_gemm(dummy, dummy, dummy, dummy, 16, N, K, fmt, None, 0, None) == status
+    assert F.lib().fp4_dequant(dummy, dummy, dummy, N, K, fmt, None) == status
+
+
+def test_gemm_argument_errors_before_any_hip_call():
+    lib = F.lib()
+    d = ctypes.c_void_p(1)
+    z = ctypes.c_void_p(0)
+    # null pointers
+    for args in ((z, d, d, d), (d, z, d, d), (d, d, z, d), (d, d, d, z)):
+        assert lib.fp4_gemm(*args, 16, 64, 64, 0, None, 0, None) == 1
+    # negative / huge m
+    assert lib.fp4_gemm(d, d, d, d, -1, 64, 64, 0, None, 0, None) == 2
+    assert lib.fp4_gemm(d, d, d, d, (1 << 20) + 1, 64, 64, 0, None, 0, None) == 2
+    # m = 0 is a no-op, even with null pointers
+    assert lib.fp4_gemm(z, z, z, z, 0, 64, 64, 0, None, 0, None) == 0
+    # A bytes beyond the 32-bit buffer range
+    assert lib.fp4_gemm(d, d, d, d, 1 << 20, 64, 1024, 0, None, 0, None) == 2
+    # repack / unpack / dequant null pointers
+    assert lib.fp4_repack(z, d, 4, 32, 0, d, d) == 1
+    assert lib.fp4_unpack(d, d, 4, 32, 0, z, d) == 1
+    assert lib.fp4_dequant(d, z, d, 4, 32, 0, None) == 1
+    sz = ctypes.c_size_t(123)
+    assert lib.fp4_gemm_workspace_size(16, 64, 64, 0, None) == 1
+    assert lib.fp4_gemm_workspace_size(16, 64, 64, 0, ctypes.byref(sz)) == 0
+
+
+def test_python_binding_validation():
+    codes, scales = _rand_weights(4, 64, 0, 1)
+    with pytest.raises(ValueError):
+        F.repack(codes[:, :8], scales, 4, 64, 0)
+    with pytest.raises(F.Fp4Error) as e:
+        F.repack_size(4, 24, 0)
+    assert e.value.status == 2

@@ -99,8 +99,8 @@ def cpu_baseline(decode_layers_probs):
     rows = 8192
     codes, scales = p.codes[:rows], p.scales[:rows]
     reps, times = 0, []
-    t_end = time.perf_counter() + 12.0
-    while reps < 3 and (reps == 0 or time.perf_counter() < t_end):
+    t_start = time.perf_counter()
+    while reps < 3 or (time.perf_counter() - t_start < 10.0 and reps < 30):
         t0 = time.perf_counter()
         oracle.gemm_reference(p.a_bits, codes, scales, p.K, p.fmt)
         times.append(time.perf_counter() - t0)
@@ -173,7 +173,7 @@ def main():
     # per-layer launch times (outside the timed step loop; each layer alone)
     per_layer = {}
     for i, l in enumerate(layers):
-        n = 2 * l.R
+        n = max(20, 2 * l.R)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for s in range(n):

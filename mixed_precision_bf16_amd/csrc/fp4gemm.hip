@@ -27,9 +27,12 @@
 //    at most 6 significant bits) and keeps the upper halves (exact BF16).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "../../include/fp4gemm.h"
 #include "layout.h"
@@ -81,42 +84,26 @@ __device__ __forceinline__ u32x4 dequant_mxfp4(uint32_t w, float sexp) {
     return o;
 }
 
-// Scale words of one lane for one 512-K scale block (layout.h).
-template <int FMT> struct ScaleWord;
-template <> struct ScaleWord<0> { typedef u32x2 type; };
-template <> struct ScaleWord<1> { typedef uint32_t type; };
-
-// Scale operand for chunk C (0..3) of the block and half H (0: dwords 0-1,
-// 1: dwords 2-3 of the lane's 32 K).  NVFP4: OCP E4M3 -> FP32 via the
-// hardware FP8 convert (OCP encoding on gfx950, checked on the device).
-template <int C, int H>
-__device__ __forceinline__ float nv_scale(u32x2 s) {
-    constexpr int byte = 2 * C + H;
-    const uint32_t word = (byte < 4) ? s.x : s.y;
-    return __builtin_amdgcn_cvt_f32_fp8((int)word, byte & 3);
+// Scales of one lane for one 512-K scale block: 16 bytes; byte 4 c + i is the
+// scale of MFMA step i of chunk c (layout.h).  Lane byte offset inside the
+// block: NVFP4 r * 32 + (j / 2) * 16, MXFP4 r * 16.
+template <int FMT>
+__device__ __forceinline__ int scale_lane_offset(int r, int j) {
+    return FMT == 0 ? r * 32 + (j >> 1) * 16 : r * 16;
 }
-template <int C>
-__device__ __forceinline__ float mx_scale(uint32_t s) {
-    return __uint_as_float(((s >> (8 * C)) & 0xFFu) << 23);
-}
+template <int FMT>
+constexpr int scale_block_bytes() { return FMT == 0 ? 512 : 256; }
 
 // Dequantize MFMA step I (dword I of the lane's 16 bytes) of chunk C.
+// NVFP4: OCP E4M3 -> FP32 with the hardware FP8 convert (OCP encoding on
+// gfx950, checked on the device).  MXFP4: the E8M0 byte becomes the exponent
+// field of the FP32 scale operand.
 template <int FMT, int C, int I>
-__device__ __forceinline__ u32x4 dequant_step(const u32x4& w, const typename ScaleWord<FMT>::type& s) {
+__device__ __forceinline__ u32x4 dequant_step(const u32x4& w, const u32x4& s) {
     if constexpr (FMT == 0) {
-        return dequant_nvfp4(w[I], nv_scale<C, I / 2>(s));
+        return dequant_nvfp4(w[I], __builtin_amdgcn_cvt_f32_fp8((int)s[C], I));
     } else {
-        return dequant_mxfp4(w[I], mx_scale<C>(s));
-    }
-}
-
-template <int FMT>
-__device__ __forceinline__ typename ScaleWord<FMT>::type load_scales(const uint8_t* __restrict__ sq, size_t blk,
-                                                                     int lane) {
-    if constexpr (FMT == 0) {
-        return reinterpret_cast<const u32x2*>(sq)[blk * kLanes + lane];
-    } else {
-        return reinterpret_cast<const uint32_t*>(sq)[blk * kLanes + lane];
+        return dequant_mxfp4(w[I], __uint_as_float(((s[C] >> (8 * I)) & 0xFFu) << 23));
     }
 }
 
@@ -153,29 +140,83 @@ __device__ __forceinline__ void store_frag(uint16_t* __restrict__ C, const f32x4
 
 // ------------------------------------------------------------ skinny GEMM
 // Small m (<= 16*MB): each workgroup owns TN n-tiles (16 rows each) and its NW
-// waves split K; every wave streams its share of the tiles' 1 KiB code blocks
-// straight into VGPRs, reads the matching activation fragments (64
-// contiguous bytes per lane per chunk) with ranged buffer loads, and the
-// partial 16x16 products are summed across the waves through LDS in a fixed
-// order (deterministic).
-template <int FMT, int MB, int TN, int NW>
+// waves split K into contiguous ranges of 512-K scale blocks.  Every wave
+// streams its tiles' 1 KiB code blocks straight into VGPRs one scale block
+// ahead of the block it is multiplying (so 4*TN KiB per wave are in flight
+// while it computes), reads the matching activation fragments (64 contiguous
+// bytes per lane per chunk) one chunk ahead with ranged buffer loads, and the
+// partial 16x16 products of the waves are summed through LDS in a fixed order
+// (deterministic).  Chunk offsets live in scalar registers; only the chunk
+// holding the end of K masks lanes.
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufWord3);
+}
+
+template <int FMT>
+__device__ __forceinline__ u32x4 load_scale_block(__amdgpu_buffer_rsrc_t r, int soff_lane, int sb) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, soff_lane, sb * scale_block_bytes<FMT>(), 0);
+}
+
+template <int FMT, int MB, int C, int I>
+__device__ __forceinline__ void mma_step(const u32x4& w, const u32x4& s,
+                                         const u32x4 (&a)[MB][4], f32x4 (&acc)[MB]) {
+    const u32x4 wf = dequant_step<FMT, C, I>(w, s);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_bf16(wf, a[mb][I], acc[mb]);
+}
+
+template <int FMT, int MB, int C>
+__device__ __forceinline__ void mma_chunk(const u32x4& w, const u32x4& s,
+                                          const u32x4 (&a)[MB][4], f32x4 (&acc)[MB]) {
+    mma_step<FMT, MB, C, 0>(w, s, a, acc);
+    mma_step<FMT, MB, C, 1>(w, s, a, acc);
+    mma_step<FMT, MB, C, 2>(w, s, a, acc);
+    mma_step<FMT, MB, C, 3>(w, s, a, acc);
+}
+
+// Activation fragments of chunk b for the lane: rows mb*16 + r, K = 128 b + 32 i + 8 j.
+// KTAIL (K not a multiple of 512): lanes whose 8 K-values lie at or past K read
+// zeros through an out-of-range offset instead of the next row's data.
+template <int MB, bool KTAIL>
+__device__ __forceinline__ void load_a_chunk(__amdgpu_buffer_rsrc_t ra, const uint32_t (&arow)[MB], int b, int j,
+                                             int K, u32x4 (&a)[MB][4]) {
+    const int kb = b * kChunkK + j * 8;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = kb + 32 * i;
+            const uint32_t off = arow[mb] + (uint32_t)k * 2u;
+            a[mb][i] = load_a(ra, (!KTAIL || k < K) ? off : kOutOfRange);
+        }
+}
+
+template <int FMT, int MB, int TN, int NW, bool KTAIL>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny(const uint16_t* __restrict__ A, const u32x4* __restrict__ wq,
                                                       const uint8_t* __restrict__ sq, uint16_t* __restrict__ C,
                                                       int M, int N, int K, int KB, int SB, int NT) {
-    typedef typename ScaleWord<FMT>::type SW;
+    typedef u32x4 SW;
+    constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();  // per tile per scale block
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int r = lane & 15, j = lane >> 4;
     const int tile0 = blockIdx.x * TN;
+    const int soff = scale_lane_offset<FMT>(r, j);
 
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, M * K * 2, kBufWord3);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(M * K * 2));
     uint32_t arow[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) arow[mb] = (uint32_t)((mb * 16 + r) * K) * 2u;
 
-    int tl[TN];  // tiles past the end re-read the last tile; their stores are masked by n < N
+    // Tiles past the end re-read the last tile; their stores are masked by n < N.
+    __amdgpu_buffer_rsrc_t rw[TN], rs[TN];
 #pragma unroll
-    for (int tt = 0; tt < TN; ++tt) tl[tt] = min(tile0 + tt, NT - 1);
+    for (int tt = 0; tt < TN; ++tt) {
+        const int t = min(tile0 + tt, NT - 1);
+        rw[tt] = make_rsrc(reinterpret_cast<const uint8_t*>(wq) + (size_t)t * KB * 1024, (uint32_t)KB * 1024u);
+        rs[tt] = make_rsrc(sq + (size_t)t * SB * kScaleBlockBytes, (uint32_t)(SB * kScaleBlockBytes));
+    }
 
     f32x4 acc[TN][MB];
 #pragma unroll
@@ -183,44 +224,59 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny(const uint16_t* __restric
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Software pipeline over 128-K chunks, three chunks deep: the code block
+    // and activation fragments of chunk c+3 are issued into register slot
+    // (c+3) % 4 before chunk c is multiplied.  Vector-memory loads complete in
+    // issue order, and every wait is for loads issued three steps earlier, so
+    // no wait ever covers a younger prefetch.  Scale blocks are fetched one
+    // block ahead.  The tail re-reads the wave's last chunk (a cache hit)
+    // instead of branching.
     const int sb0 = (wave * SB) / NW, sb1 = ((wave + 1) * SB) / NW;
-    for (int sb = sb0; sb < sb1; ++sb) {
-        SW sc[TN];
+    if (sb0 < sb1) {
+        const int clast = 4 * sb1 - 1;
+        u32x4 wr[4][TN];
+        u32x4 ar[4][MB][4];
+        SW sc[TN], scn[TN];
+        auto issue = [&](auto slot_c, int chunk) {
+            constexpr int S = decltype(slot_c)::value;
+            chunk = min(chunk, clast);
 #pragma unroll
-        for (int tt = 0; tt < TN; ++tt) sc[tt] = load_scales<FMT>(sq, (size_t)tl[tt] * SB + sb, lane);
+            for (int tt = 0; tt < TN; ++tt)
+                wr[S][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, 0);
+            load_a_chunk<MB, KTAIL>(ra, arow, chunk, j, K, ar[S]);
+        };
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int b = sb * 4 + c;
-            u32x4 w[TN];
+        for (int tt = 0; tt < TN; ++tt) sc[tt] = load_scale_block<FMT>(rs[tt], soff, sb0);
+        issue(std::integral_constant<int, 0>{}, 4 * sb0 + 0);
+        issue(std::integral_constant<int, 1>{}, 4 * sb0 + 1);
+        issue(std::integral_constant<int, 2>{}, 4 * sb0 + 2);
+        for (int sb = sb0; sb < sb1; ++sb) {
+            const int base = 4 * sb;
+            const int nsb = min(sb + 1, sb1 - 1);
+            issue(std::integral_constant<int, 3>{}, base + 3);
 #pragma unroll
-            for (int tt = 0; tt < TN; ++tt) w[tt] = wq[((size_t)tl[tt] * KB + b) * kLanes + lane];
-            const int kb = b * kChunkK + j * 32;
-            u32x4 a[MB][4];
+            for (int tt = 0; tt < TN; ++tt) scn[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 0>(wr[0][tt], sc[tt], ar[0], acc[tt]);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(std::integral_constant<int, 0>{}, base + 4);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int k = kb + 8 * i;
-                    a[mb][i] = load_a(ra, k < K ? arow[mb] + (uint32_t)k * 2u : kOutOfRange);
-                }
+            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 1>(wr[1][tt], sc[tt], ar[1], acc[tt]);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(std::integral_constant<int, 1>{}, base + 5);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int tt = 0; tt < TN; ++tt) {
-                u32x4 wf[4];
-                switch (c) {  // c is a compile-time constant after unrolling
-                    case 0: wf[0] = dequant_step<FMT, 0, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 0, 1>(w[tt], sc[tt]);
-                            wf[2] = dequant_step<FMT, 0, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 0, 3>(w[tt], sc[tt]); break;
-                    case 1: wf[0] = dequant_step<FMT, 1, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 1, 1>(w[tt], sc[tt]);
-                            wf[2] = dequant_step<FMT, 1, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 1, 3>(w[tt], sc[tt]); break;
-                    case 2: wf[0] = dequant_step<FMT, 2, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 2, 1>(w[tt], sc[tt]);
-                            wf[2] = dequant_step<FMT, 2, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 2, 3>(w[tt], sc[tt]); break;
-                    default: wf[0] = dequant_step<FMT, 3, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 3, 1>(w[tt], sc[tt]);
-                             wf[2] = dequant_step<FMT, 3, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 3, 3>(w[tt], sc[tt]); break;
-                }
+            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 2>(wr[2][tt], sc[tt], ar[2], acc[tt]);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(std::integral_constant<int, 2>{}, base + 6);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 3>(wr[3][tt], sc[tt], ar[3], acc[tt]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = mfma_bf16(wf[i], a[mb][i], acc[tt][mb]);
-            }
+            for (int tt = 0; tt < TN; ++tt) sc[tt] = scn[tt];
         }
     }
 
@@ -258,7 +314,7 @@ template <int FMT>
 __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A, const u32x4* __restrict__ wq,
                                                  const uint8_t* __restrict__ sq, uint16_t* __restrict__ C, int M,
                                                  int N, int K, int KB, int SB, int NT) {
-    typedef typename ScaleWord<FMT>::type SW;
+    typedef u32x4 SW;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTiledBM * 256];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -281,7 +337,9 @@ __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A
     for (int sb = 0; sb < SB; ++sb) {
         SW sc[4];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) sc[tt] = load_scales<FMT>(sq, (size_t)tl[tt] * SB + sb, lane);
+        for (int tt = 0; tt < 4; ++tt)
+            sc[tt] = *reinterpret_cast<const u32x4*>(sq + ((size_t)tl[tt] * SB + sb) * scale_block_bytes<FMT>() +
+                                                     scale_lane_offset<FMT>(r, j));
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int b = sb * 4 + c;
@@ -305,7 +363,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A
                 const int row = wm * 64 + mb * 16 + r;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int col = j * 4 + i;
+                    const int col = i * 4 + j;  // 16-byte column of K = 32 i + 8 j
                     a[mb][i] = *reinterpret_cast<const u32x4*>(lds_a + row * 256 + ((col ^ (row & 15)) << 4));
                 }
             }
@@ -343,12 +401,13 @@ __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A
 template <int FMT>
 __global__ __launch_bounds__(64) void dequant_kernel(const u32x4* __restrict__ wq, const uint8_t* __restrict__ sq,
                                                      uint16_t* __restrict__ W, int N, int K, int KB, int SB) {
-    typedef typename ScaleWord<FMT>::type SW;
+    typedef u32x4 SW;
     const int t = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x, r = lane & 15, j = lane >> 4;
     const int n = t * kTileN + r;
     const u32x4 w = wq[((size_t)t * KB + b) * kLanes + lane];
-    const SW s = load_scales<FMT>(sq, (size_t)t * SB + b / 4, lane);
+    const SW s = *reinterpret_cast<const u32x4*>(sq + ((size_t)t * SB + b / 4) * scale_block_bytes<FMT>() +
+                                                 scale_lane_offset<FMT>(r, j));
     u32x4 o[4];
     switch (b & 3) {
         case 0: o[0] = dequant_step<FMT, 0, 0>(w, s); o[1] = dequant_step<FMT, 0, 1>(w, s);
@@ -363,7 +422,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(const u32x4* __restrict__ w
     if (n >= N) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int k = b * kChunkK + j * 32 + 8 * i;
+        const int k = b * kChunkK + 32 * i + 8 * j;
         if (k < K) *reinterpret_cast<u32x4*>(W + (size_t)n * K + k) = o[i];
     }
 }
@@ -396,19 +455,79 @@ static int64_t a_row_block(int64_t M) {
     return kTiledBM;
 }
 
+// Skinny-kernel shape: TN n-tiles per workgroup, NW waves splitting K.
+struct SkinnyShape {
+    int tn, nw;
+};
+
+// Tuning override "TN,NW" from FP4GEMM_SKINNY (read once; used by sweeps).
+static SkinnyShape skinny_override() {
+    static const SkinnyShape ov = [] {
+        SkinnyShape s{0, 0};
+        const char* e = getenv("FP4GEMM_SKINNY");
+        if (e) sscanf(e, "%d,%d", &s.tn, &s.nw);
+        return s;
+    }();
+    return ov;
+}
+
+// Measured on MI355X over the Llama-3-70B decode shapes (m = 16): many
+// n-tiles favour fewer, wider waves; long K favours more waves per tile.
+static SkinnyShape pick_skinny(int MB, int NT, int SB) {
+    SkinnyShape ov = skinny_override();
+    if (ov.tn > 0) return ov;
+    if (MB > 1) return {1, 4};
+    if (NT >= 2048) return {4, 2};
+    if (SB >= 32) return {2, 4};
+    if (NT >= 640) return {4, 4};
+    return {2, 4};
+}
+
+#define FP4_SKINNY_CASE(MB_, TN_, NW_)                                                                   \
+    if (sh.tn == TN_ && sh.nw == NW_) {                                                                  \
+        gemm_skinny<FMT, MB_, TN_, NW_, false><<<dim3((NT + TN_ - 1) / TN_), dim3(64 * NW_), 0, s>>>(    \
+            A, wq, sq, C, M, N, K, KB, SB, NT);                                                          \
+        return true;                                                                                     \
+    }
+
 template <int FMT>
-static void launch_gemm(const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, int M, int N, int K,
-                        int KB, int SB, int NT, hipStream_t s) {
-    if (M <= 16) {
-        gemm_skinny<FMT, 1, 1, 4><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
-    } else if (M <= 32) {
-        gemm_skinny<FMT, 2, 1, 4><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+static bool launch_skinny(int MB, SkinnyShape sh, const uint16_t* A, const u32x4* wq, const uint8_t* sq,
+                          uint16_t* C, int M, int N, int K, int KB, int SB, int NT, hipStream_t s) {
+    if (MB == 1) {
+        FP4_SKINNY_CASE(1, 1, 2) FP4_SKINNY_CASE(1, 1, 4) FP4_SKINNY_CASE(1, 1, 8)
+        FP4_SKINNY_CASE(1, 2, 2) FP4_SKINNY_CASE(1, 2, 4) FP4_SKINNY_CASE(1, 2, 8)
+        FP4_SKINNY_CASE(1, 4, 2) FP4_SKINNY_CASE(1, 4, 4) FP4_SKINNY_CASE(1, 4, 8)
+    } else if (MB == 2) {
+        FP4_SKINNY_CASE(2, 1, 4) FP4_SKINNY_CASE(2, 1, 8) FP4_SKINNY_CASE(2, 2, 4) FP4_SKINNY_CASE(2, 2, 8)
+    } else {
+        FP4_SKINNY_CASE(4, 1, 4)
+    }
+    return false;
+}
+#undef FP4_SKINNY_CASE
+
+template <int FMT>
+static int launch_gemm(const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, int M, int N, int K,
+                       int KB, int SB, int NT, hipStream_t s) {
+    if (M <= 64 && K % kScaleBlockK != 0) {  // ragged K: masked activation loads
+        if (M <= 16)
+            gemm_skinny<FMT, 1, 1, 4, true><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+        else if (M <= 32)
+            gemm_skinny<FMT, 2, 1, 4, true><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+        else
+            gemm_skinny<FMT, 4, 1, 4, true><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
     } else if (M <= 64) {
-        gemm_skinny<FMT, 4, 1, 4><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+        const int MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+        SkinnyShape sh = pick_skinny(MB, NT, SB);
+        if (!launch_skinny<FMT>(MB, sh, A, wq, sq, C, M, N, K, KB, SB, NT, s)) {
+            sh = SkinnyShape{1, 4};  // an override naming no compiled shape falls back to the default
+            launch_skinny<FMT>(MB, sh, A, wq, sq, C, M, N, K, KB, SB, NT, s);
+        }
     } else {
         dim3 grid((NT + kTiledBNT - 1) / kTiledBNT, (M + kTiledBM - 1) / kTiledBM);
         gemm_tiled<FMT><<<grid, dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
     }
+    return FP4_OK;
 }
 
 }  // namespace fp4

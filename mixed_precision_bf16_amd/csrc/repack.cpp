@@ -4,7 +4,7 @@
 // FP4 Mixed-Precision Inference on AMD GPUs", section "Efficient
 // dequantization through preprocessing") and of the petit-kernel PyPI page
 // ("Techniques and performance": weights are shuffled offline).  Here it is a
-// pure byte permutation (plus zero padding) into the layout of layout.h, so it
+// pure permutation of 4-byte words (plus zero padding) into the layout of layout.h, so it
 // is exactly invertible and never changes a value.
 #include <string.h>
 
@@ -27,7 +27,7 @@ extern "C" const char* fp4_status_string(int status) {
     }
 }
 
-// Shared by the host and device entry points (declared in fp4gemm_internal.h).
+// Shared by the host and the device entry points (fp4gemm.hip declares it).
 int fp4_check_weight_shape(int64_t N, int64_t K, int format) {
     if (format != FP4_NVFP4 && format != FP4_MXFP4) return FP4_ERR_FORMAT;
     const int64_t G = group_of(format);
@@ -66,11 +66,8 @@ extern "C" int fp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N
     memset(sq, 0, size_t(Np * Kp / G));
     for (int64_t n = 0; n < N; ++n) {
         const uint8_t* row = codes + n * (K / 2);
-        // one lane's 16 bytes cover 32 consecutive k of the row
-        for (int64_t k = 0; k < K; k += 32) {
-            const int64_t len = (K - k >= 32) ? 16 : (K - k) / 2;
-            memcpy(wq + wq_offset(n, k, KB), row + k / 2, size_t(len));
-        }
+        // one packed dword holds 8 consecutive k of the row
+        for (int64_t k = 0; k < K; k += 8) memcpy(wq + wq_offset(n, k, KB), row + k / 2, 4);
         const uint8_t* srow = scales + n * ng;
         for (int64_t g = 0; g < ng; ++g) sq[sq_offset(n, g * G, SB, format)] = srow[g];
     }
@@ -88,10 +85,7 @@ extern "C" int fp4_unpack(const uint8_t* wq, const uint8_t* sq, int64_t N, int64
     const int64_t KB = Kp / kChunkK, SB = Kp / kScaleBlockK;
     for (int64_t n = 0; n < N; ++n) {
         uint8_t* row = codes + n * (K / 2);
-        for (int64_t k = 0; k < K; k += 32) {
-            const int64_t len = (K - k >= 32) ? 16 : (K - k) / 2;
-            memcpy(row + k / 2, wq + wq_offset(n, k, KB), size_t(len));
-        }
+        for (int64_t k = 0; k < K; k += 8) memcpy(row + k / 2, wq + wq_offset(n, k, KB), 4);
         uint8_t* srow = scales + n * ng;
         for (int64_t g = 0; g < ng; ++g) srow[g] = sq[sq_offset(n, g * G, SB, format)];
     }

@@ -63,18 +63,48 @@ def test_repack_roundtrip_and_padding(N, K, fmt):
     assert np.array_equal(np.bincount(sq, minlength=256), sb)
 
 
-def test_repack_is_a_permutation_of_16_byte_lane_blocks():
-    # Every run of 16 source bytes (32 consecutive k of one row) lands intact
-    # in one 16-byte slot of the packed codes.
+def test_repack_is_a_permutation_of_source_dwords():
+    # Every source dword (8 consecutive k of one row) lands intact in one
+    # 4-byte-aligned slot of the packed codes.
     N, K = 20, 1024
-    codes = np.arange(N * K // 2, dtype=np.uint64).astype(np.uint8).reshape(N, K // 2)
     codes = ((np.arange(N * K // 2) * 2654435761) >> 7).astype(np.uint8).reshape(N, K // 2)
     scales = np.full((N, K // 16), 0x38, np.uint8)
     wq, _ = F.repack(codes, scales, N, K, 0)
-    slots = {bytes(wq[i:i + 16]) for i in range(0, wq.size, 16)}
+    slots = {bytes(wq[i:i + 4]) for i in range(0, wq.size, 4)}
     for n in range(N):
-        for k in range(0, K, 32):
-            assert bytes(codes[n, k // 2:k // 2 + 16]) in slots
+        for k in range(0, K, 8):
+            assert bytes(codes[n, k // 2:k // 2 + 4]) in slots
+
+
+def _packed_code_offset(n, k, K):
+    """Documented packed-code layout: 1 KiB block per (16-row tile, 128-K chunk);
+    lane 16 j + r holds 16 bytes; its dword i covers k = 128 b + 32 i + 8 j .. +7."""
+    KB = -(-K // 512) * 4
+    t, r = divmod(n, 16)
+    b, kk = divmod(k, 128)
+    i, j = kk // 32, (kk % 32) // 8
+    return ((t * KB + b) * 64 + 16 * j + r) * 16 + 4 * i + (k % 8) // 2
+
+
+def _packed_scale_offset(n, k, K, fmt):
+    SB = -(-K // 512)
+    t, r = divmod(n, 16)
+    sb, c, i = k // 512, (k % 512) // 128, (k % 128) // 32
+    if fmt == 0:
+        return (t * SB + sb) * 512 + r * 32 + ((k % 32) // 16) * 16 + 4 * c + i
+    return (t * SB + sb) * 256 + r * 16 + 4 * c + i
+
+
+@pytest.mark.parametrize("N,K,fmt", [(19, 1040, 0), (33, 1056, 1)])
+def test_repack_matches_documented_layout(N, K, fmt):
+    codes, scales = _rand_weights(N, K, fmt, seed=77)
+    G = 16 if fmt == 0 else 32
+    wq, sq = F.repack(codes, scales, N, K, fmt)
+    for n in range(N):
+        for k in range(0, K, 2):
+            assert wq[_packed_code_offset(n, k, K)] == codes[n, k // 2]
+        for g in range(K // G):
+            assert sq[_packed_scale_offset(n, g * G, K, fmt)] == scales[n, g]
 
 
 def test_repack_synthetic_config_roundtrip():

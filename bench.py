@@ -70,13 +70,14 @@ class Layer:
         self.sq = [sq_d] + [sq_d.clone() for _ in range(self.R - 1)]
 
 
-def make_call(F, torch, layer, A, C, r):
+def make_call(F, torch, layer, A, C, r, ws):
     """Pre-marshalled fp4_gemm call on torch's current stream."""
     lib = F.lib()
     stream = F._c_vp(torch.cuda.current_stream().cuda_stream)
     m = A.shape[0]
+    ws_bytes = ws.numel() if ws is not None else 0
     args = (F._dev_ptr(A), F._dev_ptr(layer.wq[r]), F._dev_ptr(layer.sq[r]), F._dev_ptr(C), m, layer.N, layer.K,
-            layer.fmt, None, 0, stream)
+            layer.fmt, F._dev_ptr(ws), ws_bytes, stream)
     fn = lib.fp4_gemm
 
     def call():
@@ -138,7 +139,8 @@ def main():
     m = 16
     A = [torch.from_numpy(p.a_bits.view(np.int16)).to(dev).view(torch.bfloat16) for p in probs]
     C = [torch.empty((m, l.N), dtype=torch.bfloat16, device=dev) for l in layers]
-    calls = [[make_call(F, torch, l, A[i], C[i], r) for r in range(l.R)] for i, l in enumerate(layers)]
+    WS = [F.new_workspace(m, l.N, l.K, l.fmt, device=dev) for l in layers]
+    calls = [[make_call(F, torch, l, A[i], C[i], r, WS[i]) for r in range(l.R)] for i, l in enumerate(layers)]
     bytes_step = sum(algorithmic_bytes(m, l.N, l.K, l.G) for l in layers)
     dom = 2  # gate_up
 
@@ -194,7 +196,8 @@ def main():
         for i, l in enumerate(layers):
             a = torch.from_numpy(rng.standard_normal((mp, l.K), dtype=np.float32)).to(torch.bfloat16).to(dev)
             c = torch.empty((mp, l.N), dtype=torch.bfloat16, device=dev)
-            pc = [make_call(F, torch, l, a, c, r) for r in range(l.R)]
+            ws = F.new_workspace(mp, l.N, l.K, l.fmt, device=dev)
+            pc = [make_call(F, torch, l, a, c, r, ws) for r in range(l.R)]
             for s in range(5):
                 pc[s % l.R]()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

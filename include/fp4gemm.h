@@ -98,7 +98,9 @@ int fp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K
 int fp4_unpack(const uint8_t* wq, const uint8_t* sq, int64_t N, int64_t K, int format,
                uint8_t* codes, uint8_t* scales);
 
-/* Workspace bytes fp4_gemm needs for this problem (0 when none). */
+/* Workspace bytes fp4_gemm needs for this problem.  Every kernel of this
+ * version works without scratch memory, so this is 0; the workspace
+ * arguments keep scratch caller-owned should a later kernel need it. */
 int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int format, size_t* bytes);
 
 /* Y = A . dequant(W)^T on `stream` (a hipStream_t; NULL = default stream).
@@ -107,9 +109,7 @@ int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int format, size_t*
  *   sq  device, packed scales from fp4_repack
  *   C   device, BF16 [m][N] row-major, contiguous; every element is written
  *   workspace / workspace_bytes: device scratch of at least
- *       fp4_gemm_workspace_size bytes (may be NULL when that size is 0);
- *       its contents on entry do not matter.  One workspace must not be used
- *       by two launches that may run at the same time.
+ *       fp4_gemm_workspace_size bytes (may be NULL when that size is 0).
  * m == 0 is a no-op returning FP4_OK.  Asynchronous: returns once the kernels
  * are queued; faults surface at the caller's next synchronization.
  * Accumulation is FP32; the output is rounded to BF16 to nearest even. */

@@ -52,6 +52,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // parts; an offset at or past the buffer's byte range reads zero.
 constexpr int kBufWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kXcdCount = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 // ------------------------------------------------------------------ dequant
 // Keep the upper 16 bits of two FP32 values (exact when both are BF16 values).
@@ -303,96 +304,158 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny(const uint16_t* __restric
 }
 
 // ------------------------------------------------------------- tiled GEMM
-// Larger m: a 256-thread workgroup computes a 128 (m) x 128 (n) tile; its four
-// waves form a 2 x 2 grid of 64 x 64 sub-tiles (4 x 4 MFMA fragments each).
-// Per 128-K chunk the activation tile (128 x 128 BF16, 32 KiB) is staged in
-// LDS with an XOR swizzle of its 16-byte columns by row, and each wave loads
-// the 1 KiB code blocks of its four n-tiles directly into VGPRs.
-constexpr int kTiledBM = 128, kTiledBNT = 8;  // m rows, n-tiles per workgroup
-
-template <int FMT>
+// Larger m.  A 256-thread workgroup computes a BM x BN output tile with its
+// four waves in a WM x WN grid; a wave owns MBW 16-row blocks of m and TNW
+// 16-row tiles of n.  Per 128-K chunk:
+//   * the activation tile (BM rows x 128 K, BF16) lives in LDS, double
+//     buffered, with its 16-byte columns XOR-swizzled by row so that both the
+//     16-byte writes and the fragment reads are free of bank conflicts (the
+//     Petit blog, "Mastering the memory hierarchy": permuted LDS layout);
+//   * the next chunk's activations and code blocks are loaded into registers
+//     while the current chunk is multiplied (activations first, so the wait
+//     before they are written to LDS never covers the code-block prefetch);
+//   * barriers fence LDS only, so they never drain the prefetch.
+// Work items are ordered so that each XCD gets a contiguous band of n-tiles
+// (all m-tiles of it): the band's codes are fetched by one L2 only and the
+// activations stay L2-resident per XCD (the blog's topology-aware partition).
+template <int FMT, int WM, int WN, int MBW, int TNW, bool KTAIL>
 __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A, const u32x4* __restrict__ wq,
                                                  const uint8_t* __restrict__ sq, uint16_t* __restrict__ C, int M,
                                                  int N, int K, int KB, int SB, int NT) {
-    typedef u32x4 SW;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTiledBM * 256];
+    static_assert(WM * WN == 4, "four waves");
+    constexpr int BM = WM * MBW * 16;  // m rows per workgroup
+    constexpr int BNT = WN * TNW;      // n-tiles per workgroup
+    constexpr int kBuf = BM * 256;     // one LDS activation buffer (BM x 128 K x 2 B)
+    constexpr int kStage = BM / 16;    // 16-byte activation pieces per thread per chunk
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kBuf];
+
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, j = lane >> 4;
-    const int wm = wave & 1, wn = wave >> 1;
-    const int m0 = blockIdx.y * kTiledBM;
-    const int tile0 = blockIdx.x * kTiledBNT + wn * 4;
+    const int wm = wave % WM, wn = wave / WM;
 
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, M * K * 2, kBufWord3);
-    int tl[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) tl[tt] = min(tile0 + tt, NT - 1);
+    // XCD-banded work order
+    const int MT = (M + BM - 1) / BM, NG = (NT + BNT - 1) / BNT;
+    const int total = MT * NG;
+    int L = blockIdx.x;
+    if (total % kXcdCount == 0) L = (blockIdx.x % kXcdCount) * (total / kXcdCount) + blockIdx.x / kXcdCount;
+    const int mt = L % MT, ng = L / MT;
+    const int m0 = mt * BM;
+    const int tile0 = ng * BNT + wn * TNW;
 
-    f32x4 acc[4][4];
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(M * K * 2));
+    constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();
+    const int soff = scale_lane_offset<FMT>(r, j);
+    __amdgpu_buffer_rsrc_t rw[TNW], rs[TNW];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < TNW; ++tt) {
+        const int t = min(tile0 + tt, NT - 1);
+        rw[tt] = make_rsrc(reinterpret_cast<const uint8_t*>(wq) + (size_t)t * KB * 1024, (uint32_t)KB * 1024u);
+        rs[tt] = make_rsrc(sq + (size_t)t * SB * kScaleBlockBytes, (uint32_t)(SB * kScaleBlockBytes));
+    }
 
-    for (int sb = 0; sb < SB; ++sb) {
-        SW sc[4];
+    // activation staging: piece q of this thread = (row, 16-byte column)
+    uint32_t aoff[kStage];
+    int lds_off[kStage];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-            sc[tt] = *reinterpret_cast<const u32x4*>(sq + ((size_t)tl[tt] * SB + sb) * scale_block_bytes<FMT>() +
-                                                     scale_lane_offset<FMT>(r, j));
+    for (int q = 0; q < kStage; ++q) {
+        const int idx = tid + 256 * q;
+        const int row = idx >> 4, col = idx & 15;
+        aoff[q] = (uint32_t)((m0 + row) * K + col * 8) * 2u;
+        lds_off[q] = row * 256 + ((col ^ (row & 15)) << 4);
+    }
+    auto load_stage = [&](int b, u32x4 (&st)[kStage]) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int b = sb * 4 + c;
-            // stage A[m0 .. m0+127][128 b .. 128 b + 127] into LDS
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int p = tid + 256 * q;
-                const int row = p >> 4, col = p & 15;
-                const int k = b * kChunkK + col * 8;
-                const uint32_t off = k < K ? (uint32_t)((m0 + row) * K + k) * 2u : kOutOfRange;
-                const u32x4 v = load_a(ra, off);
-                *reinterpret_cast<u32x4*>(lds_a + row * 256 + ((col ^ (row & 15)) << 4)) = v;
-            }
-            u32x4 w[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) w[tt] = wq[((size_t)tl[tt] * KB + b) * kLanes + lane];
-            __syncthreads();
-            u32x4 a[4][4];
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const int row = wm * 64 + mb * 16 + r;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int col = i * 4 + j;  // 16-byte column of K = 32 i + 8 j
-                    a[mb][i] = *reinterpret_cast<const u32x4*>(lds_a + row * 256 + ((col ^ (row & 15)) << 4));
-                }
-            }
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                u32x4 wf[4];
-                switch (c) {
-                    case 0: wf[0] = dequant_step<FMT, 0, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 0, 1>(w[tt], sc[tt]);
-                            wf[2] = dequant_step<FMT, 0, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 0, 3>(w[tt], sc[tt]); break;
-                    case 1: wf[0] = dequant_step<FMT, 1, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 1, 1>(w[tt], sc[tt]);
-                            wf[2] = dequant_step<FMT, 1, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 1, 3>(w[tt], sc[tt]); break;
-                    case 2: wf[0] = dequant_step<FMT, 2, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 2, 1>(w[tt], sc[tt]);
-                            wf[2] = dequant_step<FMT, 2, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 2, 3>(w[tt], sc[tt]); break;
-                    default: wf[0] = dequant_step<FMT, 3, 0>(w[tt], sc[tt]); wf[1] = dequant_step<FMT, 3, 1>(w[tt], sc[tt]);
-                             wf[2] = dequant_step<FMT, 3, 2>(w[tt], sc[tt]); wf[3] = dequant_step<FMT, 3, 3>(w[tt], sc[tt]); break;
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int mb = 0; mb < 4; ++mb) acc[tt][mb] = mfma_bf16(wf[i], a[mb][i], acc[tt][mb]);
-            }
-            __syncthreads();
+        for (int q = 0; q < kStage; ++q) {
+            const int col = ((tid + 256 * q) & 15);
+            const int k = b * kChunkK + col * 8;
+            const uint32_t off = aoff[q] + (uint32_t)(b * kChunkK) * 2u;
+            st[q] = load_a(ra, (!KTAIL || k < K) ? off : kOutOfRange);
         }
+    };
+    auto store_stage = [&](int buf, const u32x4 (&st)[kStage]) {
+#pragma unroll
+        for (int q = 0; q < kStage; ++q) *reinterpret_cast<u32x4*>(lds_a + buf * kBuf + lds_off[q]) = st[q];
+    };
+    auto lds_barrier = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    f32x4 acc[TNW][MBW];
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // multiply chunk b (activations in LDS buffer buf) with code blocks w
+    auto compute = [&](auto cc, int buf, const u32x4 (&w)[TNW], const u32x4 (&sc)[TNW]) {
+        constexpr int CC = decltype(cc)::value;
+        const uint8_t* base = lds_a + buf * kBuf;
+        auto step = [&](auto ii) {
+            constexpr int I = decltype(ii)::value;
+            u32x4 a[MBW];
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb) {
+                const int row = wm * MBW * 16 + mb * 16 + r;
+                const int col = 4 * I + j;
+                a[mb] = *reinterpret_cast<const u32x4*>(base + row * 256 + ((col ^ (row & 15)) << 4));
+            }
+#pragma unroll
+            for (int tt = 0; tt < TNW; ++tt) {
+                const u32x4 wf = dequant_step<FMT, CC, I>(w[tt], sc[tt]);
+#pragma unroll
+                for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = mfma_bf16(wf, a[mb], acc[tt][mb]);
+            }
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+    };
+
+    const int last = KB - 1;
+    u32x4 st[kStage];
+    u32x4 w0[TNW], w1[TNW], sc[TNW], scn[TNW];
+    load_stage(0, st);
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt) {
+        w0[tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, 0, 0);
+        sc[tt] = load_scale_block<FMT>(rs[tt], soff, 0);
+    }
+    store_stage(0, st);
+    lds_barrier();
+    // chunk pairs (b even in w0, b odd in w1); a scale block is 4 chunks
+    for (int sb = 0; sb < SB; ++sb) {
+        const int nsb = min(sb + 1, SB - 1);
+        auto half = [&](auto cc, const u32x4 (&wc)[TNW], u32x4 (&wn)[TNW]) {
+            constexpr int CC = decltype(cc)::value;
+            const int b = 4 * sb + CC;
+            const int bn = min(b + 1, last);
+            load_stage(bn, st);
+#pragma unroll
+            for (int tt = 0; tt < TNW; ++tt) {
+                wn[tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, bn * 1024, 0);
+                if constexpr (CC == 3) scn[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
+            }
+            compute(cc, b & 1, wc, sc);
+            store_stage((b + 1) & 1, st);
+            lds_barrier();
+        };
+        half(std::integral_constant<int, 0>{}, w0, w1);
+        half(std::integral_constant<int, 1>{}, w1, w0);
+        half(std::integral_constant<int, 2>{}, w0, w1);
+        half(std::integral_constant<int, 3>{}, w1, w0);
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt) sc[tt] = scn[tt];
     }
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int tt = 0; tt < TNW; ++tt)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-            store_frag(C, acc[tt][mb], m0 + wm * 64 + mb * 16 + r, (tile0 + tt) * kTileN + 4 * j, M, N);
+        for (int mb = 0; mb < MBW; ++mb)
+            store_frag(C, acc[tt][mb], m0 + wm * MBW * 16 + mb * 16 + r, (tile0 + tt) * kTileN + 4 * j, M, N);
 }
 
 // ------------------------------------------------------------ debug dequant
@@ -447,12 +510,12 @@ static int launch_status() {
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
-// Row block the kernel for this m reads A in (A offsets are 32-bit).
+// Row block the kernels for this m read A in (A offsets are 32-bit).
 static int64_t a_row_block(int64_t M) {
     if (M <= 16) return 16;
     if (M <= 32) return 32;
     if (M <= 64) return 64;
-    return kTiledBM;
+    return 256;  // largest tiled m-block
 }
 
 // Skinny-kernel shape: TN n-tiles per workgroup, NW waves splitting K.
@@ -506,6 +569,54 @@ static bool launch_skinny(int MB, SkinnyShape sh, const uint16_t* A, const u32x4
 }
 #undef FP4_SKINNY_CASE
 
+// Tiled-kernel shape: WM x WN waves, MBW m-blocks and TNW n-tiles per wave.
+struct TiledShape {
+    int wm, wn, mbw, tnw;
+};
+
+static TiledShape tiled_override() {
+    static const TiledShape ov = [] {
+        TiledShape t{0, 0, 0, 0};
+        const char* e = getenv("FP4GEMM_TILED");
+        if (e) sscanf(e, "%d,%d,%d,%d", &t.wm, &t.wn, &t.mbw, &t.tnw);
+        return t;
+    }();
+    return ov;
+}
+
+// Measured on MI355X over the Llama-3-70B prefill shapes (m = 256): one wave
+// over all 128 rows of the block amortizes each dequantized code over 128
+// products; wide-N shapes take two n-tiles per wave.
+static TiledShape pick_tiled(int M, int NT) {
+    (void)M;
+    TiledShape ov = tiled_override();
+    if (ov.wm > 0) return ov;
+    return NT >= 640 ? TiledShape{1, 4, 8, 2} : TiledShape{1, 4, 8, 1};
+}
+
+template <int FMT, int WM, int WN, int MBW, int TNW>
+static void launch_tiled_t(const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, int M, int N, int K,
+                           int KB, int SB, int NT, hipStream_t s) {
+    constexpr int BM = WM * MBW * 16, BNT = WN * TNW;
+    const int grid = ((M + BM - 1) / BM) * ((NT + BNT - 1) / BNT);
+    if (K % kScaleBlockK == 0)
+        gemm_tiled<FMT, WM, WN, MBW, TNW, false><<<dim3(grid), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+    else
+        gemm_tiled<FMT, WM, WN, MBW, TNW, true><<<dim3(grid), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+}
+
+template <int FMT>
+static void launch_tiled(TiledShape t, const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, int M,
+                         int N, int K, int KB, int SB, int NT, hipStream_t s) {
+#define FP4_TILED_CASE(WM_, WN_, MBW_, TNW_)                                                         \
+    if (t.wm == WM_ && t.wn == WN_ && t.mbw == MBW_ && t.tnw == TNW_)                                \
+        return launch_tiled_t<FMT, WM_, WN_, MBW_, TNW_>(A, wq, sq, C, M, N, K, KB, SB, NT, s);
+    FP4_TILED_CASE(1, 4, 8, 1) FP4_TILED_CASE(1, 4, 8, 2) FP4_TILED_CASE(1, 4, 4, 1) FP4_TILED_CASE(1, 4, 4, 2)
+    FP4_TILED_CASE(2, 2, 4, 4) FP4_TILED_CASE(2, 2, 4, 2)
+#undef FP4_TILED_CASE
+    launch_tiled_t<FMT, 1, 4, 8, 1>(A, wq, sq, C, M, N, K, KB, SB, NT, s);  // shape not compiled: default
+}
+
 template <int FMT>
 static int launch_gemm(const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, int M, int N, int K,
                        int KB, int SB, int NT, hipStream_t s) {
@@ -524,8 +635,7 @@ static int launch_gemm(const uint16_t* A, const u32x4* wq, const uint8_t* sq, ui
             launch_skinny<FMT>(MB, sh, A, wq, sq, C, M, N, K, KB, SB, NT, s);
         }
     } else {
-        dim3 grid((NT + kTiledBNT - 1) / kTiledBNT, (M + kTiledBM - 1) / kTiledBM);
-        gemm_tiled<FMT><<<grid, dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+        launch_tiled<FMT>(pick_tiled(M, NT), A, wq, sq, C, M, N, K, KB, SB, NT, s);
     }
     return FP4_OK;
 }
@@ -545,14 +655,14 @@ extern "C" int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int form
 
 extern "C" int fp4_gemm(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
                         int format, void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     int st = fp4_check_weight_shape(N, K, format);
     if (st != FP4_OK) return st;
     if (m < 0 || m > (int64_t(1) << 20)) return FP4_ERR_SHAPE;
     if (m == 0) return FP4_OK;
     if (!A || !wq || !sq || !C) return FP4_ERR_NULL;
     if (round_up(m, a_row_block(m)) * K * 2 >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
+    (void)workspace;
+    (void)workspace_bytes;
     st = check_device();
     if (st != FP4_OK) return st;
     const int64_t Np = padded_n(N), Kp = padded_k(K);

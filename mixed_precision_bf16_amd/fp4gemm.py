@@ -137,6 +137,13 @@ def _stream_handle(stream):
     return _c_vp(stream.cuda_stream)
 
 
+def new_workspace(m: int, N: int, K: int, fmt: int, device="cuda"):
+    """A zero-filled workspace for fp4_gemm of this shape (None if none is needed)."""
+    import torch
+    nbytes = workspace_size(m, N, K, fmt)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
 def gemm(A, wq, sq, N: int, K: int, fmt: int, out=None, workspace=None, stream=None):
     """Y = A . dequant(W)^T.  A: bf16 CUDA [m][K]; wq, sq: uint8 CUDA (packed).
     Returns (or fills) a bf16 CUDA tensor [m][N]."""
@@ -158,7 +165,7 @@ def gemm(A, wq, sq, N: int, K: int, fmt: int, out=None, workspace=None, stream=N
         raise ValueError("out must be a contiguous bfloat16 tensor [m][N]")
     wsb = workspace_size(m, N, K, fmt)
     if wsb and workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=A.device)
+        workspace = torch.zeros(wsb, dtype=torch.uint8, device=A.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().fp4_gemm(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), m, N, K, fmt,
                           _dev_ptr(workspace), ws_bytes, _stream_handle(stream)), "fp4_gemm")

@@ -179,3 +179,9 @@ def test_python_binding_validation():
     with pytest.raises(F.Fp4Error) as e:
         F.repack_size(4, 24, 0)
     assert e.value.status == 2
+
+
+def test_workspace_size_is_zero_for_every_kernel():
+    for m, N, K, fmt in ((16, 8192, 8192, 0), (1, 57344, 8192, 1), (256, 8192, 28672, 0), (33, 100, 544, 1)):
+        assert F.workspace_size(m, N, K, fmt) == 0
+    assert F.new_workspace(16, 8192, 8192, 0) is None

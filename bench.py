@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--prefill-launches", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 256 MiB device-to-device copy first (known bytes for HBM counter scaling)")
     return ap.parse_args()
 
 
@@ -131,6 +133,15 @@ def main():
     F.lib()
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy: 268435456 bytes read, 268435456 bytes written")
 
     t0 = time.time()
     probs = [synth.make_problem(1, si, 0) for si in range(4)]

@@ -225,19 +225,22 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny(const uint16_t* __restric
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Software pipeline over 128-K chunks, three chunks deep: the code block
-    // and activation fragments of chunk c+3 are issued into register slot
-    // (c+3) % 4 before chunk c is multiplied.  Vector-memory loads complete in
-    // issue order, and every wait is for loads issued three steps earlier, so
-    // no wait ever covers a younger prefetch.  Scale blocks are fetched one
-    // block ahead.  The tail re-reads the wave's last chunk (a cache hit)
-    // instead of branching.
+    // Software pipeline over 128-K chunks, three chunks deep: register slot
+    // c % 4 holds the code blocks and activation fragments of chunk c; at the
+    // step that multiplies chunk c, chunk c+3 is issued into slot (c+3) % 4.
+    // Vector-memory loads complete in issue order, and every wait is for a
+    // slot filled three steps earlier, so no wait covers a younger prefetch.
+    // Scales alternate between two register sets, one 512-K block ahead, and
+    // the loop body covers two blocks so that no loaded register is copied
+    // across the loop back edge (that keeps the compiler's wait counts exact).
+    // The tail re-reads the wave's last chunk (a cache hit) instead of
+    // branching.
     const int sb0 = (wave * SB) / NW, sb1 = ((wave + 1) * SB) / NW;
     if (sb0 < sb1) {
         const int clast = 4 * sb1 - 1;
         u32x4 wr[4][TN];
         u32x4 ar[4][MB][4];
-        SW sc[TN], scn[TN];
+        SW sa[TN], sbs[TN];
         auto issue = [&](auto slot_c, int chunk) {
             constexpr int S = decltype(slot_c)::value;
             chunk = min(chunk, clast);
@@ -246,39 +249,44 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny(const uint16_t* __restric
                 wr[S][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, 0);
             load_a_chunk<MB, KTAIL>(ra, arow, chunk, j, K, ar[S]);
         };
-#pragma unroll
-        for (int tt = 0; tt < TN; ++tt) sc[tt] = load_scale_block<FMT>(rs[tt], soff, sb0);
-        issue(std::integral_constant<int, 0>{}, 4 * sb0 + 0);
-        issue(std::integral_constant<int, 1>{}, 4 * sb0 + 1);
-        issue(std::integral_constant<int, 2>{}, 4 * sb0 + 2);
-        for (int sb = sb0; sb < sb1; ++sb) {
-            const int base = 4 * sb;
-            const int nsb = min(sb + 1, sb1 - 1);
+        // one 512-K block: multiply chunks 4 sbx .. 4 sbx + 3 with scales cur,
+        // prefetch the scales of block nsb into nxt
+        auto block = [&](int sbx, const SW (&cur)[TN], SW (&nxt)[TN], int nsb) {
+            const int base = 4 * sbx;
             issue(std::integral_constant<int, 3>{}, base + 3);
 #pragma unroll
-            for (int tt = 0; tt < TN; ++tt) scn[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
+            for (int tt = 0; tt < TN; ++tt) nxt[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 0>(wr[0][tt], sc[tt], ar[0], acc[tt]);
+            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 0>(wr[0][tt], cur[tt], ar[0], acc[tt]);
             __builtin_amdgcn_sched_barrier(0);
             issue(std::integral_constant<int, 0>{}, base + 4);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 1>(wr[1][tt], sc[tt], ar[1], acc[tt]);
+            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 1>(wr[1][tt], cur[tt], ar[1], acc[tt]);
             __builtin_amdgcn_sched_barrier(0);
             issue(std::integral_constant<int, 1>{}, base + 5);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 2>(wr[2][tt], sc[tt], ar[2], acc[tt]);
+            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 2>(wr[2][tt], cur[tt], ar[2], acc[tt]);
             __builtin_amdgcn_sched_barrier(0);
             issue(std::integral_constant<int, 2>{}, base + 6);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 3>(wr[3][tt], sc[tt], ar[3], acc[tt]);
+            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 3>(wr[3][tt], cur[tt], ar[3], acc[tt]);
             __builtin_amdgcn_sched_barrier(0);
+        };
 #pragma unroll
-            for (int tt = 0; tt < TN; ++tt) sc[tt] = scn[tt];
+        for (int tt = 0; tt < TN; ++tt) sa[tt] = load_scale_block<FMT>(rs[tt], soff, sb0);
+        issue(std::integral_constant<int, 0>{}, 4 * sb0 + 0);
+        issue(std::integral_constant<int, 1>{}, 4 * sb0 + 1);
+        issue(std::integral_constant<int, 2>{}, 4 * sb0 + 2);
+        int sb = sb0;
+        for (; sb + 1 < sb1; sb += 2) {
+            block(sb, sa, sbs, sb + 1);
+            block(sb + 1, sbs, sa, min(sb + 2, sb1 - 1));
         }
+        if (sb < sb1) block(sb, sa, sbs, sb);  // odd block count
     }
 
     if constexpr (NW > 1) {

@@ -250,7 +250,7 @@ def main():
                    "m": m, "weights": "nvfp4 (E2M1 codes, E4M3 scale per 16)", "activations": "bf16",
                    "accumulate": "fp32", "rotating_weight_copies": {l.name: l.R for l in layers}},
         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "gemm_skinny (gate_up, m=16)", "bound": "hbm", "achieved": round(dom_gbs, 1),
+        "roofline": {"kernel": "gemm_decode (gate_up, m=16)", "bound": "hbm", "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_us, 2), "traffic": None},
         "layers": per_layer,

@@ -59,7 +59,8 @@ enum {
 enum {
     FP4_OK = 0,
     FP4_ERR_NULL = 1,      /* a required pointer is NULL */
-    FP4_ERR_SHAPE = 2,     /* N < 1, K < G, K % G != 0, m < 0, or a size over the limits below */
+    FP4_ERR_SHAPE = 2,     /* N < 1, K < G, K % G != 0, m < 0, a size over the limits below,
+                              or (fp4_gemm) a device pointer not 16-byte aligned */
     FP4_ERR_FORMAT = 3,    /* format is neither FP4_NVFP4 nor FP4_MXFP4 */
     FP4_ERR_VALUE = 4,     /* fp4_repack: a scale byte is negative or NaN */
     FP4_ERR_WORKSPACE = 5, /* workspace smaller than fp4_gemm_workspace_size */
@@ -98,9 +99,13 @@ int fp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K
 int fp4_unpack(const uint8_t* wq, const uint8_t* sq, int64_t N, int64_t K, int format,
                uint8_t* codes, uint8_t* scales);
 
-/* Workspace bytes fp4_gemm needs for this problem.  Every kernel of this
- * version works without scratch memory, so this is 0; the workspace
- * arguments keep scratch caller-owned should a later kernel need it. */
+/* Workspace bytes fp4_gemm needs for this problem (a pure function of its
+ * arguments; no device is queried).  For m <= 64 the library may split K over
+ * S workgroups (split-K, the Petit blog's section "Detailed performance
+ * analysis" motivates it for the skinny decode case): each writes FP32
+ * partial sums of its K range and a second kernel adds them in a fixed order,
+ * so the size is S * m * N * 4 bytes, or 0 when no split is chosen.  The
+ * contents need no initialization and are not preserved between calls. */
 int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int format, size_t* bytes);
 
 /* Y = A . dequant(W)^T on `stream` (a hipStream_t; NULL = default stream).
@@ -108,11 +113,17 @@ int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int format, size_t*
  *   wq  device, packed codes from fp4_repack (uploaded by the caller)
  *   sq  device, packed scales from fp4_repack
  *   C   device, BF16 [m][N] row-major, contiguous; every element is written
- *   workspace / workspace_bytes: device scratch of at least
- *       fp4_gemm_workspace_size bytes (may be NULL when that size is 0).
+ *   workspace / workspace_bytes: device scratch, 16-byte aligned, of at
+ *       least fp4_gemm_workspace_size bytes (may be NULL when that size is
+ *       0); FP4_ERR_WORKSPACE otherwise.  Calls that may run concurrently
+ *       (different streams) need separate workspaces.
+ * A, wq, sq and C must be 16-byte aligned (the kernels use 16-byte vector
+ * loads and 8-byte stores).
  * m == 0 is a no-op returning FP4_OK.  Asynchronous: returns once the kernels
  * are queued; faults surface at the caller's next synchronization.
- * Accumulation is FP32; the output is rounded to BF16 to nearest even. */
+ * Accumulation is FP32; the output is rounded to BF16 to nearest even.
+ * Results are deterministic: the same inputs give the same bits on every
+ * call (fixed summation order, no atomics). */
 int fp4_gemm(const void* A, const void* wq, const void* sq, void* C,
              int64_t m, int64_t N, int64_t K, int format,
              void* workspace, size_t workspace_bytes, void* stream);

@@ -31,6 +31,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -52,6 +53,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // parts; an offset at or past the buffer's byte range reads zero.
 constexpr int kBufWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache-policy operand of buffer loads that stream data read once (the
+// weight codes and scales): the nontemporal hint.
+constexpr int kLoadStream = 2;
 constexpr int kXcdCount = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 // ------------------------------------------------------------------ dequant
@@ -87,10 +91,10 @@ __device__ __forceinline__ u32x4 dequant_mxfp4(uint32_t w, float sexp) {
 
 // Scales of one lane for one 512-K scale block: 16 bytes; byte 4 c + i is the
 // scale of MFMA step i of chunk c (layout.h).  Lane byte offset inside the
-// block: NVFP4 r * 32 + (j / 2) * 16, MXFP4 r * 16.
+// block: NVFP4 (j / 2) * 256 + r * 16, MXFP4 r * 16.
 template <int FMT>
 __device__ __forceinline__ int scale_lane_offset(int r, int j) {
-    return FMT == 0 ? r * 32 + (j >> 1) * 16 : r * 16;
+    return FMT == 0 ? (j >> 1) * 256 + r * 16 : r * 16;
 }
 template <int FMT>
 constexpr int scale_block_bytes() { return FMT == 0 ? 512 : 256; }
@@ -139,78 +143,74 @@ __device__ __forceinline__ void store_frag(uint16_t* __restrict__ C, const f32x4
     }
 }
 
-// ------------------------------------------------------------ skinny GEMM
-// Small m (<= 16*MB): each workgroup owns TN n-tiles (16 rows each) and its NW
-// waves split K into contiguous ranges of 512-K scale blocks.  Every wave
-// streams its tiles' 1 KiB code blocks straight into VGPRs one scale block
-// ahead of the block it is multiplying (so 4*TN KiB per wave are in flight
-// while it computes), reads the matching activation fragments (64 contiguous
-// bytes per lane per chunk) one chunk ahead with ranged buffer loads, and the
-// partial 16x16 products of the waves are summed through LDS in a fixed order
-// (deterministic).  Chunk offsets live in scalar registers; only the chunk
-// holding the end of K masks lanes.
-
+// ------------------------------------------------------------ buffer loads
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufWord3);
 }
 
 template <int FMT>
 __device__ __forceinline__ u32x4 load_scale_block(__amdgpu_buffer_rsrc_t r, int soff_lane, int sb) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, soff_lane, sb * scale_block_bytes<FMT>(), 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, soff_lane, sb * scale_block_bytes<FMT>(), kLoadStream);
 }
 
-template <int FMT, int MB, int C, int I>
-__device__ __forceinline__ void mma_step(const u32x4& w, const u32x4& s,
-                                         const u32x4 (&a)[MB][4], f32x4 (&acc)[MB]) {
-    const u32x4 wf = dequant_step<FMT, C, I>(w, s);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_bf16(wf, a[mb][I], acc[mb]);
-}
-
-template <int FMT, int MB, int C>
-__device__ __forceinline__ void mma_chunk(const u32x4& w, const u32x4& s,
-                                          const u32x4 (&a)[MB][4], f32x4 (&acc)[MB]) {
-    mma_step<FMT, MB, C, 0>(w, s, a, acc);
-    mma_step<FMT, MB, C, 1>(w, s, a, acc);
-    mma_step<FMT, MB, C, 2>(w, s, a, acc);
-    mma_step<FMT, MB, C, 3>(w, s, a, acc);
-}
-
-// Activation fragments of chunk b for the lane: rows mb*16 + r, K = 128 b + 32 i + 8 j.
-// KTAIL (K not a multiple of 512): lanes whose 8 K-values lie at or past K read
-// zeros through an out-of-range offset instead of the next row's data.
-template <int MB, bool KTAIL>
-__device__ __forceinline__ void load_a_chunk(__amdgpu_buffer_rsrc_t ra, const uint32_t (&arow)[MB], int b, int j,
-                                             int K, u32x4 (&a)[MB][4]) {
-    const int kb = b * kChunkK + j * 8;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = kb + 32 * i;
-            const uint32_t off = arow[mb] + (uint32_t)k * 2u;
-            a[mb][i] = load_a(ra, (!KTAIL || k < K) ? off : kOutOfRange);
-        }
-}
-
-template <int FMT, int MB, int TN, int NW, bool KTAIL>
-__global__ __launch_bounds__(64 * NW) void gemm_skinny(const uint16_t* __restrict__ A, const u32x4* __restrict__ wq,
-                                                      const uint8_t* __restrict__ sq, uint16_t* __restrict__ C,
-                                                      int M, int N, int K, int KB, int SB, int NT) {
+// ------------------------------------------------------------ decode GEMM
+// Small m (<= 16*MB) with the activations shared through LDS.  A workgroup has
+// NWK groups of NWN waves.  The waves of one group cover the same K range and
+// different n-tiles (TN each), so one activation chunk in LDS feeds
+// TN*NWN tiles: each activation byte crosses the L1/L2 path once per
+// workgroup instead of once per wave, and the loads that bring it in read
+// whole 128-byte lines (8 rows x 128 bytes per wave instruction).  The NWK
+// groups split the workgroup's K range and are summed through LDS in a fixed
+// order.  Narrow layers also split K over S workgroups: each writes FP32
+// partial sums to the caller's workspace and reduce_partials adds them in a
+// fixed order (no atomics, deterministic).
+//
+// Pipeline.  Code blocks stream through a four-slot register ring, three
+// 128-K chunks ahead of the multiply.  Activations move one 512-K scale block
+// at a time through two LDS buffers: at the start of block x the
+// activations of block x+1 are issued into registers (before the code blocks
+// issued during block x, so waiting for them never waits for a younger code
+// prefetch), and at the end of block x they are written to the buffer block
+// x-1 used.  One barrier per block (LDS only: the prefetches stay in flight)
+// separates those writes from the reads of block x+1 and the reads of block
+// x-1 from the writes.
+template <int FMT, int MB, int TN, int NWN, int NWK, bool KTAIL>
+__global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __restrict__ A,
+                                                             const u32x4* __restrict__ wq,
+                                                             const uint8_t* __restrict__ sq,
+                                                             uint16_t* __restrict__ C, float* __restrict__ P, int M,
+                                                             int N, int K, int KB, int SB, int NT, int S) {
     typedef u32x4 SW;
-    constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();  // per tile per scale block
+    constexpr int kRows = 16 * MB;  // activation rows; one 1 KiB load per row per block
+    // Activation load instructions per wave per block.  When NWN does not
+    // divide the row count, the surplus loads repeat the last row: they
+    // write the same bytes to the same LDS slot as its first load.
+    constexpr int QB = (kRows + NWN - 1) / NWN;
+    constexpr int kBuf = MB * 4096;  // one chunk: 16*MB rows x 128 K x 2 B
+    constexpr int kBlk = 4 * kBuf;     // one 512-K block
+    constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[NWK * 2 * kBlk];
+
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % NWN, wk = wave / NWN;
     const int r = lane & 15, j = lane >> 4;
-    const int tile0 = blockIdx.x * TN;
+    const int ks = blockIdx.x % S, grp = blockIdx.x / S;
+    const int tile0 = grp * (TN * NWN) + wn * TN;
     const int soff = scale_lane_offset<FMT>(r, j);
 
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(M * K * 2));
-    uint32_t arow[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) arow[mb] = (uint32_t)((mb * 16 + r) * K) * 2u;
+    // K range of the workgroup and of this wave's group, in 512-K scale blocks.
+    // Every group runs nblk blocks so that all waves meet at every barrier; a
+    // group with fewer blocks skips the multiply of the extra ones.
+    const int wsb0 = (ks * SB) / S, wsb1 = ((ks + 1) * SB) / S;
+    const int span = wsb1 - wsb0;
+    const int sb0 = wsb0 + (wk * span) / NWK, sb1 = wsb0 + ((wk + 1) * span) / NWK;
+    const int nblk = (span + NWK - 1) / NWK;
+    const int own = sb1 - sb0;
+    const int sbmax = own > 0 ? sb1 - 1 : wsb0;         // last block this group may read
+    const int cmax = own > 0 ? 4 * sb1 - 1 : 4 * wsb0;  // last chunk this group may read
 
-    // Tiles past the end re-read the last tile; their stores are masked by n < N.
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(M * K * 2));
     __amdgpu_buffer_rsrc_t rw[TN], rs[TN];
 #pragma unroll
     for (int tt = 0; tt < TN; ++tt) {
@@ -219,96 +219,188 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny(const uint16_t* __restric
         rs[tt] = make_rsrc(sq + (size_t)t * SB * kScaleBlockBytes, (uint32_t)(SB * kScaleBlockBytes));
     }
 
+    // Activations in LDS, per 128-K chunk: the 16-byte fragment of MFMA step
+    // I, m-block mb, lane (j, r) sits in slot 16 j + (r ^ (4 I + j)) of the
+    // 1 KiB run (I, mb).  The XOR spreads the 16 octets of one row over all
+    // 16 bank groups, so the row-contiguous writes below and the fragment
+    // reads are both free of bank conflicts.
+    // Load u of this wave brings row q = wn + NWN u of a 512-K block: lane l
+    // reads the 16 contiguous bytes at k = 512 sb + 8 l (chunk l / 16, octet
+    // l % 16), so one instruction is 1 KiB of one row.
+    const int a_oct = lane & 15;
+    const int a_base = (lane >> 4) * kBuf + (((a_oct >> 2) * MB) * 64 + 16 * (a_oct & 3)) * 16;
+    // Rows at or past m are neither loaded nor stored: they only feed MFMA
+    // output columns that are never written back.
+    uint32_t aoff[QB];
+    int ldst[QB];
+    bool alive[QB];
+#pragma unroll
+    for (int u = 0; u < QB; ++u) {
+        const int row = min(wn + NWN * u, kRows - 1);
+        alive[u] = row < M;
+        aoff[u] = (uint32_t)(row * K + 8 * lane) * 2u;
+        ldst[u] = a_base + ((row >> 4) * 64 + ((row & 15) ^ a_oct)) * 16;
+    }
+    uint8_t* const ring = lds_a + wk * 2 * kBlk;
+
     f32x4 acc[TN][MB];
 #pragma unroll
     for (int tt = 0; tt < TN; ++tt)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Software pipeline over 128-K chunks, three chunks deep: register slot
-    // c % 4 holds the code blocks and activation fragments of chunk c; at the
-    // step that multiplies chunk c, chunk c+3 is issued into slot (c+3) % 4.
-    // Vector-memory loads complete in issue order, and every wait is for a
-    // slot filled three steps earlier, so no wait covers a younger prefetch.
-    // Scales alternate between two register sets, one 512-K block ahead, and
-    // the loop body covers two blocks so that no loaded register is copied
-    // across the loop back edge (that keeps the compiler's wait counts exact).
-    // The tail re-reads the wave's last chunk (a cache hit) instead of
-    // branching.
-    const int sb0 = (wave * SB) / NW, sb1 = ((wave + 1) * SB) / NW;
-    if (sb0 < sb1) {
-        const int clast = 4 * sb1 - 1;
-        u32x4 wr[4][TN];
-        u32x4 ar[4][MB][4];
-        SW sa[TN], sbs[TN];
-        auto issue = [&](auto slot_c, int chunk) {
-            constexpr int S = decltype(slot_c)::value;
-            chunk = min(chunk, clast);
+    u32x4 wr[4][TN];
+    u32x4 ar[QB];
+    SW sa[TN], sbs[TN];
+    // activations of block sbx into registers
+    auto a_issue = [&](int sbx) {
+        const bool in_k = !KTAIL || sbx * kScaleBlockK + 8 * lane < K;
 #pragma unroll
-            for (int tt = 0; tt < TN; ++tt)
-                wr[S][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, 0);
-            load_a_chunk<MB, KTAIL>(ra, arow, chunk, j, K, ar[S]);
-        };
-        // one 512-K block: multiply chunks 4 sbx .. 4 sbx + 3 with scales cur,
-        // prefetch the scales of block nsb into nxt
-        auto block = [&](int sbx, const SW (&cur)[TN], SW (&nxt)[TN], int nsb) {
-            const int base = 4 * sbx;
-            issue(std::integral_constant<int, 3>{}, base + 3);
-#pragma unroll
-            for (int tt = 0; tt < TN; ++tt) nxt[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 0>(wr[0][tt], cur[tt], ar[0], acc[tt]);
-            __builtin_amdgcn_sched_barrier(0);
-            issue(std::integral_constant<int, 0>{}, base + 4);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 1>(wr[1][tt], cur[tt], ar[1], acc[tt]);
-            __builtin_amdgcn_sched_barrier(0);
-            issue(std::integral_constant<int, 1>{}, base + 5);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 2>(wr[2][tt], cur[tt], ar[2], acc[tt]);
-            __builtin_amdgcn_sched_barrier(0);
-            issue(std::integral_constant<int, 2>{}, base + 6);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int tt = 0; tt < TN; ++tt) mma_chunk<FMT, MB, 3>(wr[3][tt], cur[tt], ar[3], acc[tt]);
-            __builtin_amdgcn_sched_barrier(0);
-        };
-#pragma unroll
-        for (int tt = 0; tt < TN; ++tt) sa[tt] = load_scale_block<FMT>(rs[tt], soff, sb0);
-        issue(std::integral_constant<int, 0>{}, 4 * sb0 + 0);
-        issue(std::integral_constant<int, 1>{}, 4 * sb0 + 1);
-        issue(std::integral_constant<int, 2>{}, 4 * sb0 + 2);
-        int sb = sb0;
-        for (; sb + 1 < sb1; sb += 2) {
-            block(sb, sa, sbs, sb + 1);
-            block(sb + 1, sbs, sa, min(sb + 2, sb1 - 1));
+        for (int u = 0; u < QB; ++u) {
+            const uint32_t off = aoff[u] + (uint32_t)sbx * (kScaleBlockK * 2);
+            if (alive[u]) ar[u] = load_a(ra, in_k ? off : kOutOfRange);
         }
-        if (sb < sb1) block(sb, sa, sbs, sb);  // odd block count
-    }
+    };
+    auto a_store = [&](int buf) {
+        uint8_t* dst = ring + buf * kBlk;
+#pragma unroll
+        for (int u = 0; u < QB; ++u)
+            if (alive[u]) *reinterpret_cast<u32x4*>(dst + ldst[u]) = ar[u];
+    };
+    auto w_issue = [&](auto slot_c, int chunk) {
+        constexpr int SL = decltype(slot_c)::value;
+        chunk = min(chunk, cmax);
+#pragma unroll
+        for (int tt = 0; tt < TN; ++tt)
+            wr[SL][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, kLoadStream);
+    };
+    auto lds_barrier = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    // multiply chunk T of the block in LDS buffer buf with code slot T
+    auto compute = [&](auto slot_c, const uint8_t* blk_base, const SW (&sc)[TN]) {
+        constexpr int T = decltype(slot_c)::value;
+        const uint8_t* base = blk_base + T * kBuf;
+        auto step = [&](auto ii) {
+            constexpr int I = decltype(ii)::value;
+            u32x4 a[MB];
+            const int slot = 16 * j + (r ^ (4 * I + j));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                a[mb] = *reinterpret_cast<const u32x4*>(base + ((I * MB + mb) * 64 + slot) * 16);
+#pragma unroll
+            for (int tt = 0; tt < TN; ++tt) {
+                const u32x4 wf = dequant_step<FMT, T, I>(wr[T][tt], sc[tt]);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = mfma_bf16(wf, a[mb], acc[tt][mb]);
+            }
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+    };
+    auto pstep = [&](auto slot_c, int base, bool valid, const uint8_t* blk_base, const SW (&cur)[TN]) {
+        constexpr int T = decltype(slot_c)::value;
+        w_issue(std::integral_constant<int, (T + 3) % 4>{}, base + T + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        if (valid) compute(slot_c, blk_base, cur);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // one 512-K block (x = blk, LDS buffer PAR = blk % 2): chunks 4 (sb0 + blk)
+    // .. +3 with scales cur; prefetches the next block's scales into nxt and
+    // its activations into registers, and stores those to the other buffer.
+    auto block = [&](auto par_c, int blk, const SW (&cur)[TN], SW (&nxt)[TN]) {
+        constexpr int PAR = decltype(par_c)::value;
+        const int base = 4 * (sb0 + blk);
+        const bool valid = blk < own;
+        const int nsb = min(sb0 + blk + 1, sbmax);
+        lds_barrier();
+        a_issue(nsb);
+#pragma unroll
+        for (int tt = 0; tt < TN; ++tt) nxt[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
+        const uint8_t* blk_base = ring + PAR * kBlk;
+        pstep(std::integral_constant<int, 0>{}, base, valid, blk_base, cur);
+        pstep(std::integral_constant<int, 1>{}, base, valid, blk_base, cur);
+        pstep(std::integral_constant<int, 2>{}, base, valid, blk_base, cur);
+        pstep(std::integral_constant<int, 3>{}, base, valid, blk_base, cur);
+        a_store(1 - PAR);
+    };
 
-    if constexpr (NW > 1) {
-        __shared__ f32x4 red[(NW - 1) * TN * MB * kLanes];
-        if (wave > 0) {
+    const int c0 = 4 * sb0;
+    a_issue(min(sb0, sbmax));
+#pragma unroll
+    for (int tt = 0; tt < TN; ++tt) sa[tt] = load_scale_block<FMT>(rs[tt], soff, min(sb0, sbmax));
+    w_issue(std::integral_constant<int, 0>{}, c0);
+    w_issue(std::integral_constant<int, 1>{}, c0 + 1);
+    w_issue(std::integral_constant<int, 2>{}, c0 + 2);
+    a_store(0);
+    int blk = 0;
+    for (; blk + 1 < nblk; blk += 2) {
+        block(std::integral_constant<int, 0>{}, blk, sa, sbs);
+        block(std::integral_constant<int, 1>{}, blk + 1, sbs, sa);
+    }
+    if (blk < nblk) block(std::integral_constant<int, 0>{}, blk, sa, sbs);
+
+    if constexpr (NWK > 1) {
+        __shared__ f32x4 red[(NWK - 1) * NWN * TN * MB * kLanes];
+        if (wk > 0) {
 #pragma unroll
             for (int tt = 0; tt < TN; ++tt)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) red[(((wave - 1) * TN + tt) * MB + mb) * kLanes + lane] = acc[tt][mb];
+                for (int mb = 0; mb < MB; ++mb)
+                    red[((((wk - 1) * NWN + wn) * TN + tt) * MB + mb) * kLanes + lane] = acc[tt][mb];
         }
         __syncthreads();
-        if (wave != 0) return;
-        for (int w = 1; w < NW; ++w)
+        if (wk != 0) return;
+        for (int g = 1; g < NWK; ++g)
 #pragma unroll
             for (int tt = 0; tt < TN; ++tt)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) acc[tt][mb] += red[(((w - 1) * TN + tt) * MB + mb) * kLanes + lane];
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[tt][mb] += red[((((g - 1) * NWN + wn) * TN + tt) * MB + mb) * kLanes + lane];
     }
 #pragma unroll
     for (int tt = 0; tt < TN; ++tt)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) store_frag(C, acc[tt][mb], mb * 16 + r, (tile0 + tt) * kTileN + 4 * j, M, N);
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
+            if (P == nullptr) {
+                store_frag(C, acc[tt][mb], m, n0, M, N);
+            } else if (m < M) {
+                float* dst = P + ((size_t)ks * M + m) * N + n0;
+                if ((N & 3) == 0 && n0 + 3 < N) {
+                    *reinterpret_cast<f32x4*>(dst) = acc[tt][mb];
+                } else {
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + e < N) dst[e] = acc[tt][mb][e];
+                }
+            }
+        }
+}
+
+// Y = sum over s of the S partial products P[s][M][N] (in order s = 0, 1, ...),
+// rounded to BF16.  Four consecutive elements of the flattened [M][N] array
+// per thread.
+__global__ __launch_bounds__(256) void reduce_partials(const float* __restrict__ P, uint16_t* __restrict__ C,
+                                                       int64_t total, int S) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= total) return;
+    if (e + 3 < total) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(P + e);
+        for (int s = 1; s < S; ++s) v += *reinterpret_cast<const f32x4*>(P + (size_t)s * total + e);
+        u32x2 o = {pack_bf16_rne(v.x, v.y), pack_bf16_rne(v.z, v.w)};
+        *reinterpret_cast<u32x2*>(C + e) = o;
+    } else {
+        for (int64_t x = e; x < total; ++x) {
+            float v = P[x];
+            for (int s = 1; s < S; ++s) v += P[(size_t)s * total + x];
+            bf16x2 b = {(__bf16)v, (__bf16)0.f};
+            C[x] = (uint16_t)(__builtin_bit_cast(uint32_t, b) & 0xFFFF);
+        }
+    }
 }
 
 // ------------------------------------------------------------- tiled GEMM
@@ -526,56 +618,145 @@ static int64_t a_row_block(int64_t M) {
     return 256;  // largest tiled m-block
 }
 
-// Skinny-kernel shape: TN n-tiles per workgroup, NW waves splitting K.
-struct SkinnyShape {
-    int tn, nw;
+// Decode-kernel shape: TN n-tiles per wave, NWN waves per K group, NWK K
+// groups per workgroup, K split over S workgroups (S > 1 needs a workspace).
+struct DecodeShape {
+    int tn, nwn, nwk, s;
 };
 
-// Tuning override "TN,NW" from FP4GEMM_SKINNY (read once; used by sweeps).
-static SkinnyShape skinny_override() {
-    static const SkinnyShape ov = [] {
-        SkinnyShape s{0, 0};
-        const char* e = getenv("FP4GEMM_SKINNY");
-        if (e) sscanf(e, "%d,%d", &s.tn, &s.nw);
-        return s;
+static DecodeShape decode_override() {
+    static const DecodeShape ov = [] {
+        DecodeShape d{0, 0, 0, 0};
+        const char* e = getenv("FP4GEMM_DECODE");
+        if (e) sscanf(e, "%d,%d,%d,%d", &d.tn, &d.nwn, &d.nwk, &d.s);
+        return d;
     }();
     return ov;
 }
 
-// Measured on MI355X over the Llama-3-70B decode shapes (m = 16): many
-// n-tiles favour fewer, wider waves; long K favours more waves per tile.
-static SkinnyShape pick_skinny(int MB, int NT, int SB) {
-    SkinnyShape ov = skinny_override();
-    if (ov.tn > 0) return ov;
-    if (MB > 1) return {1, 4};
-    if (NT >= 2048) return {4, 2};
-    if (SB >= 32) return {2, 4};
-    if (NT >= 640) return {4, 4};
-    return {2, 4};
+static bool decode_compiled(int MB, const DecodeShape& d);
+
+struct DecodeCand {
+    int mb, tn, nwn, nwk;
+};
+static const DecodeCand* decode_shapes(int* count);
+
+constexpr int kCUs = 256;  // compute units of an MI355X / MI350X (gfx950)
+
+// Modelled time of one decode launch (seconds), from measurements on MI355X:
+// a compute unit streams about 22 GB/s of weights when all 256 are busy;
+// activations are L2 hits and cost about half a weight byte per real row
+// (rows past m read nothing); every workgroup pays ~1.5 us before its first
+// block arrives; a CU needs ~24 KiB of code blocks in flight (three chunks
+// ahead per wave) to cover the memory latency; a K split over S workgroups
+// adds the partial sums' round trip and one reduce launch (~5 us with its
+// launch gap).
+static double decode_cost(int fmt, int MB, int64_t M, int64_t N, int NT, int SB, const DecodeShape& d) {
+    const int g = d.tn * d.nwn;
+    const int groups = (NT + g - 1) / g;
+    const int wgs = groups * d.s;
+    const int per_cu = (wgs + kCUs - 1) / kCUs;
+    const int bpw = (SB + d.s - 1) / d.s;
+    const int waves = d.nwn * d.nwk;
+    const int resident = std::max(1, std::min(per_cu, 16 / waves));
+    const double rows = (double)std::min<int64_t>(M, 16 * MB);
+    const double tile_block = fmt == 0 ? 4608.0 : 4352.0;  // code + scale bytes per tile per 512-K block
+    const double bytes = per_cu * ((double)g * bpw * tile_block + rows * bpw * 1024.0 * 0.5);
+    double t = bytes / 22e9 + ((per_cu + resident - 1) / resident) * 1.5e-6;
+    const double inflight = (double)waves * resident * d.tn * 3.0 * 1024.0;
+    if (inflight < 24.0 * 1024.0) t *= 24.0 * 1024.0 / inflight;
+    if (d.s > 1) t += 5e-6 + 2.0 * d.s * (double)M * (double)N * 4.0 / 2e12;
+    // Ties between shapes that move the same bytes: fewer tiles per wave
+    // (shorter dependency chains) and fewer K groups (no LDS reduction) measure
+    // slightly faster.
+    return t * (1.0 + 0.03 * (d.tn - 1)) * (1.0 + 0.02 * (d.nwk - 1));
 }
 
-#define FP4_SKINNY_CASE(MB_, TN_, NW_)                                                                   \
-    if (sh.tn == TN_ && sh.nw == NW_) {                                                                  \
-        gemm_skinny<FMT, MB_, TN_, NW_, false><<<dim3((NT + TN_ - 1) / TN_), dim3(64 * NW_), 0, s>>>(    \
-            A, wq, sq, C, M, N, K, KB, SB, NT);                                                          \
-        return true;                                                                                     \
+// Shape for m <= 16 * MB: the compiled shape and K split with the least
+// modelled time (FP4GEMM_DECODE="TN,NWN,NWK,S" overrides it for tuning).
+static DecodeShape pick_decode(int fmt, int MB, int64_t M, int64_t N, int NT, int SB) {
+    DecodeShape d = decode_override();
+    if (d.tn > 0 && decode_compiled(MB, d)) {
+        d.s = d.s < 1 ? 1 : (d.s > SB ? SB : d.s);
+        return d;
     }
+    int count = 0;
+    const DecodeCand* c = decode_shapes(&count);
+    DecodeShape best{0, 0, 0, 1};
+    double best_t = 1e30;
+    for (int i = 0; i < count; ++i) {
+        if (c[i].mb != MB) continue;
+        for (int S : {1, 2, 4, 8, 16}) {
+            if (S > SB) break;
+            const DecodeShape cand{c[i].tn, c[i].nwn, c[i].nwk, S};
+            if (c[i].nwk > (SB + S - 1) / S) continue;  // every K group gets a block
+            const double t = decode_cost(fmt, MB, M, N, NT, SB, cand);
+            if (t < best_t) {
+                best_t = t;
+                best = cand;
+            }
+        }
+    }
+    return best;
+}
 
-template <int FMT>
-static bool launch_skinny(int MB, SkinnyShape sh, const uint16_t* A, const u32x4* wq, const uint8_t* sq,
-                          uint16_t* C, int M, int N, int K, int KB, int SB, int NT, hipStream_t s) {
-    if (MB == 1) {
-        FP4_SKINNY_CASE(1, 1, 2) FP4_SKINNY_CASE(1, 1, 4) FP4_SKINNY_CASE(1, 1, 8)
-        FP4_SKINNY_CASE(1, 2, 2) FP4_SKINNY_CASE(1, 2, 4) FP4_SKINNY_CASE(1, 2, 8)
-        FP4_SKINNY_CASE(1, 4, 2) FP4_SKINNY_CASE(1, 4, 4) FP4_SKINNY_CASE(1, 4, 8)
-    } else if (MB == 2) {
-        FP4_SKINNY_CASE(2, 1, 4) FP4_SKINNY_CASE(2, 1, 8) FP4_SKINNY_CASE(2, 2, 4) FP4_SKINNY_CASE(2, 2, 8)
-    } else {
-        FP4_SKINNY_CASE(4, 1, 4)
-    }
+static size_t decode_workspace_bytes(const DecodeShape& d, int64_t M, int64_t N) {
+    return d.s > 1 ? (size_t)d.s * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+template <int FMT, int MB, int TN, int NWN, int NWK>
+static void launch_decode_t(int S, const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, float* P,
+                            int M, int N, int K, int KB, int SB, int NT, hipStream_t s) {
+    const int groups = (NT + TN * NWN - 1) / (TN * NWN);
+    const dim3 grid(groups * S), block(64 * NWN * NWK);
+    if (K % kScaleBlockK == 0)
+        gemm_decode<FMT, MB, TN, NWN, NWK, false><<<grid, block, 0, s>>>(A, wq, sq, C, P, M, N, K, KB, SB, NT, S);
+    else
+        gemm_decode<FMT, MB, TN, NWN, NWK, true><<<grid, block, 0, s>>>(A, wq, sq, C, P, M, N, K, KB, SB, NT, S);
+}
+
+// Compiled decode shapes: X(MB, TN, NWN, NWK).
+#define FP4_DECODE_SHAPES(X)                                                                         \
+    X(1, 1, 4, 1) X(1, 2, 4, 1) X(1, 4, 4, 1) X(1, 1, 4, 2) X(1, 2, 4, 2) X(1, 4, 4, 2) X(1, 2, 2, 1)  \
+    X(1, 2, 2, 2) X(1, 4, 2, 2) X(1, 1, 4, 4) X(1, 2, 4, 4) X(1, 4, 2, 1) X(1, 2, 1, 1) X(1, 4, 1, 1)  \
+    X(1, 2, 1, 4) X(1, 4, 1, 2) X(1, 2, 7, 1) X(1, 1, 7, 2) X(1, 2, 7, 2) X(1, 1, 7, 1) X(1, 2, 5, 1)  \
+    X(1, 1, 5, 2) X(1, 2, 5, 2) X(1, 1, 8, 2) X(1, 2, 8, 1) X(1, 1, 8, 1)                              \
+    X(2, 1, 4, 1) X(2, 2, 4, 1) X(2, 1, 4, 2) X(2, 2, 4, 2) X(2, 1, 8, 1)                              \
+    X(2, 1, 8, 2) X(4, 1, 4, 1) X(4, 2, 4, 1) X(4, 1, 8, 1)
+
+static const DecodeCand* decode_shapes(int* count) {
+#define FP4_DECODE_ENTRY(MB_, TN_, NWN_, NWK_) {MB_, TN_, NWN_, NWK_},
+    static const DecodeCand table[] = {FP4_DECODE_SHAPES(FP4_DECODE_ENTRY)};
+#undef FP4_DECODE_ENTRY
+    *count = int(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+static bool decode_compiled(int MB, const DecodeShape& d) {
+#define FP4_DECODE_HAS(MB_, TN_, NWN_, NWK_) \
+    if (MB == MB_ && d.tn == TN_ && d.nwn == NWN_ && d.nwk == NWK_) return true;
+    FP4_DECODE_SHAPES(FP4_DECODE_HAS)
+#undef FP4_DECODE_HAS
     return false;
 }
-#undef FP4_SKINNY_CASE
+
+template <int FMT>
+static bool launch_decode(int MB, DecodeShape d, const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C,
+                          float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s) {
+#define FP4_DECODE_CASE(MB_, TN_, NWN_, NWK_)                                                         \
+    if (MB == MB_ && d.tn == TN_ && d.nwn == NWN_ && d.nwk == NWK_) {                                 \
+        launch_decode_t<FMT, MB_, TN_, NWN_, NWK_>(d.s, A, wq, sq, C, P, M, N, K, KB, SB, NT, s);     \
+        return true;                                                                                  \
+    }
+    FP4_DECODE_SHAPES(FP4_DECODE_CASE)
+#undef FP4_DECODE_CASE
+    return false;
+}
+
+static void launch_reduce(const float* P, uint16_t* C, int64_t total, int S, hipStream_t s) {
+    const int64_t threads = (total + 3) / 4;
+    reduce_partials<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(P, C, total, S);
+}
 
 // Tiled-kernel shape: WM x WN waves, MBW m-blocks and TNW n-tiles per wave.
 struct TiledShape {
@@ -626,26 +807,26 @@ static void launch_tiled(TiledShape t, const uint16_t* A, const u32x4* wq, const
 }
 
 template <int FMT>
-static int launch_gemm(const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, int M, int N, int K,
-                       int KB, int SB, int NT, hipStream_t s) {
-    if (M <= 64 && K % kScaleBlockK != 0) {  // ragged K: masked activation loads
-        if (M <= 16)
-            gemm_skinny<FMT, 1, 1, 4, true><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
-        else if (M <= 32)
-            gemm_skinny<FMT, 2, 1, 4, true><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
-        else
-            gemm_skinny<FMT, 4, 1, 4, true><<<dim3(NT), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
-    } else if (M <= 64) {
+static int launch_gemm(const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, void* ws, int M, int N,
+                       int K, int KB, int SB, int NT, hipStream_t s) {
+    if (M <= 64) {
         const int MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-        SkinnyShape sh = pick_skinny(MB, NT, SB);
-        if (!launch_skinny<FMT>(MB, sh, A, wq, sq, C, M, N, K, KB, SB, NT, s)) {
-            sh = SkinnyShape{1, 4};  // an override naming no compiled shape falls back to the default
-            launch_skinny<FMT>(MB, sh, A, wq, sq, C, M, N, K, KB, SB, NT, s);
-        }
-    } else {
-        launch_tiled<FMT>(pick_tiled(M, NT), A, wq, sq, C, M, N, K, KB, SB, NT, s);
+        const DecodeShape d = pick_decode(FMT, MB, M, N, NT, SB);
+        float* P = d.s > 1 ? static_cast<float*>(ws) : nullptr;
+        if (!launch_decode<FMT>(MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, s)) return FP4_ERR_SHAPE;
+        if (P) launch_reduce(P, C, (int64_t)M * N, d.s, s);
+        return FP4_OK;
     }
+    launch_tiled<FMT>(pick_tiled(M, NT), A, wq, sq, C, M, N, K, KB, SB, NT, s);
     return FP4_OK;
+}
+
+// Workspace bytes of the kernel fp4_gemm picks for this problem.
+static size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
+    if (M == 0 || M > 64) return 0;
+    const int MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    const int SB = int(padded_k(K) / kScaleBlockK), NT = int(padded_n(N) / kTileN);
+    return decode_workspace_bytes(pick_decode(fmt, MB, M, N, NT, SB), M, N);
 }
 
 }  // namespace fp4
@@ -657,7 +838,7 @@ extern "C" int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int form
     if (st != FP4_OK) return st;
     if (m < 0 || m > (int64_t(1) << 20)) return FP4_ERR_SHAPE;
     if (!bytes) return FP4_ERR_NULL;
-    *bytes = 0;
+    *bytes = gemm_workspace_bytes(m, N, K, format);
     return FP4_OK;
 }
 
@@ -668,9 +849,13 @@ extern "C" int fp4_gemm(const void* A, const void* wq, const void* sq, void* C, 
     if (m < 0 || m > (int64_t(1) << 20)) return FP4_ERR_SHAPE;
     if (m == 0) return FP4_OK;
     if (!A || !wq || !sq || !C) return FP4_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(wq) | reinterpret_cast<uintptr_t>(sq) |
+         reinterpret_cast<uintptr_t>(C)) & 15)
+        return FP4_ERR_SHAPE;
     if (round_up(m, a_row_block(m)) * K * 2 >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
-    (void)workspace;
-    (void)workspace_bytes;
+    const size_t need = gemm_workspace_bytes(m, N, K, format);
+    if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15)))
+        return FP4_ERR_WORKSPACE;
     st = check_device();
     if (st != FP4_OK) return st;
     const int64_t Np = padded_n(N), Kp = padded_k(K);
@@ -678,11 +863,12 @@ extern "C" int fp4_gemm(const void* A, const void* wq, const void* sq, void* C, 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (format == FP4_NVFP4)
-        launch_gemm<0>((const uint16_t*)A, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, int(m), int(N), int(K),
-                       KB, SB, NT, s);
+        st = launch_gemm<0>((const uint16_t*)A, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, workspace, int(m),
+                            int(N), int(K), KB, SB, NT, s);
     else
-        launch_gemm<1>((const uint16_t*)A, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, int(m), int(N), int(K),
-                       KB, SB, NT, s);
+        st = launch_gemm<1>((const uint16_t*)A, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, workspace, int(m),
+                            int(N), int(K), KB, SB, NT, s);
+    if (st != FP4_OK) return st;
     return launch_status();
 }
 

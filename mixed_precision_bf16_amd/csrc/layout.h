@@ -26,11 +26,12 @@
 //     source dwords.
 //
 //   Scales (sq), one block per (tile t, scale block sb = k / 512), SB = Kp / 512:
-//     NVFP4 (G = 16): 512 bytes; row r owns 32 bytes at r * 32, as two halves
-//       h = 0, 1 of 16 bytes; byte 4 c + i of half h is the scale of group
-//       32 sb + 8 c + 2 i + h (chunk c = 0..3 of the block, step i).  Lane
-//       (j, r) loads half h = j / 2: the scales of all 16 dwords it multiplies
-//       in the block, with one 16-byte load.
+//     NVFP4 (G = 16): 512 bytes as two halves h = 0, 1 of 256 bytes; row r
+//       owns 16 bytes at h * 256 + r * 16; byte 4 c + i of them is the scale
+//       of group 32 sb + 8 c + 2 i + h (chunk c = 0..3 of the block, step i).
+//       Lane (j, r) loads half h = j / 2: the scales of all 16 dwords it
+//       multiplies in the block, with one 16-byte load; the 16 lanes of one j
+//       read 256 contiguous bytes.
 //     MXFP4 (G = 32): 256 bytes; row r owns 16 bytes at r * 16; byte 4 c + i
 //       is the scale of group 16 sb + 4 c + i.  All four lanes j of a row
 //       load the same 16 bytes.
@@ -68,7 +69,7 @@ inline int64_t sq_offset(int64_t n, int64_t k, int64_t SB, int fmt) {
     const int64_t sb = k / kScaleBlockK, c = (k % kScaleBlockK) / kChunkK, i = (k % kChunkK) / 32;
     if (fmt == 0) {
         const int64_t h = (k % 32) / 16;
-        return (t * SB + sb) * 512 + r * 32 + h * 16 + 4 * c + i;
+        return (t * SB + sb) * 512 + h * 256 + r * 16 + 4 * c + i;
     }
     return (t * SB + sb) * 256 + r * 16 + 4 * c + i;
 }

@@ -91,7 +91,7 @@ def _packed_scale_offset(n, k, K, fmt):
     t, r = divmod(n, 16)
     sb, c, i = k // 512, (k % 512) // 128, (k % 128) // 32
     if fmt == 0:
-        return (t * SB + sb) * 512 + r * 32 + ((k % 32) // 16) * 16 + 4 * c + i
+        return (t * SB + sb) * 512 + ((k % 32) // 16) * 256 + r * 16 + 4 * c + i
     return (t * SB + sb) * 256 + r * 16 + 4 * c + i
 
 
@@ -181,7 +181,29 @@ def test_python_binding_validation():
     assert e.value.status == 2
 
 
-def test_workspace_size_is_zero_for_every_kernel():
-    for m, N, K, fmt in ((16, 8192, 8192, 0), (1, 57344, 8192, 1), (256, 8192, 28672, 0), (33, 100, 544, 1)):
-        assert F.workspace_size(m, N, K, fmt) == 0
-    assert F.new_workspace(16, 8192, 8192, 0) is None
+def test_workspace_size_is_a_split_k_partial_buffer():
+    # 0 (no K split) or S * m * N * 4 bytes with 2 <= S <= 16 and S <= K / 512,
+    # a pure function of the arguments.
+    for m, N, K, fmt in ((16, 8192, 8192, 0), (16, 57344, 8192, 0), (16, 8192, 28672, 0), (1, 8192, 28672, 1),
+                         (33, 100, 544, 1), (64, 10240, 8192, 0), (7, 1000, 8192, 0)):
+        b = F.workspace_size(m, N, K, fmt)
+        assert b == F.workspace_size(m, N, K, fmt)
+        if b:
+            S, rem = divmod(b, 4 * m * N)
+            assert rem == 0 and 2 <= S <= min(16, -(-K // 512)), (m, N, K, b)
+    for m in (0, 65, 256, 1000):
+        assert F.workspace_size(m, 8192, 8192, 0) == 0
+    assert F.new_workspace(256, 8192, 8192, 0) is None
+
+
+def test_gemm_rejects_small_or_misaligned_workspace_before_any_hip_call():
+    lib = F.lib()
+    m, K = 16, 8192
+    N = next(n for n in (10240, 8192, 1000) if F.workspace_size(m, n, K, 0) > 0)
+    need = F.workspace_size(m, N, K, 0)
+    d = ctypes.c_void_p(1 << 20)  # aligned dummy device address; never dereferenced
+    assert lib.fp4_gemm(d, d, d, d, m, N, K, 0, None, need, None) == 5
+    assert lib.fp4_gemm(d, d, d, d, m, N, K, 0, d, need - 4, None) == 5
+    assert lib.fp4_gemm(d, d, d, d, m, N, K, 0, ctypes.c_void_p((1 << 20) + 4), need, None) == 5
+    # misaligned operands
+    assert lib.fp4_gemm(ctypes.c_void_p((1 << 20) + 2), d, d, d, m, N, K, 0, d, need, None) == 2

@@ -403,30 +403,32 @@ __global__ __launch_bounds__(256) void reduce_partials(const float* __restrict__
     }
 }
 
-// ------------------------------------------------------------- tiled GEMM
-// Larger m.  A 256-thread workgroup computes a BM x BN output tile with its
-// four waves in a WM x WN grid; a wave owns MBW 16-row blocks of m and TNW
-// 16-row tiles of n.  Per 128-K chunk:
-//   * the activation tile (BM rows x 128 K, BF16) lives in LDS, double
-//     buffered, with its 16-byte columns XOR-swizzled by row so that both the
-//     16-byte writes and the fragment reads are free of bank conflicts (the
-//     Petit blog, "Mastering the memory hierarchy": permuted LDS layout);
-//   * the next chunk's activations and code blocks are loaded into registers
-//     while the current chunk is multiplied (activations first, so the wait
-//     before they are written to LDS never covers the code-block prefetch);
-//   * barriers fence LDS only, so they never drain the prefetch.
-// Work items are ordered so that each XCD gets a contiguous band of n-tiles
-// (all m-tiles of it): the band's codes are fetched by one L2 only and the
-// activations stay L2-resident per XCD (the blog's topology-aware partition).
+// ----------------------------------------------------------- prefill GEMM
+// Larger m.  A 256-thread workgroup computes a BM (m) x BN (n) tile with its
+// four waves in a WM x WN grid (a wave owns MBW 16-row m-blocks and TNW
+// n-tiles), over a K range (the whole K, or 1/S of it with FP32 partials).
+// Per 128-K chunk c:
+//   issue the activations of chunk c+2 into register set c % 2 and the code
+//   blocks of chunk c+3 into ring slot (c+3) % 4 (scales one 512-K block
+//   ahead), multiply chunk c from LDS buffer c % 2 and ring slot c % 4, write
+//   the activations of chunk c+1 (issued one step earlier) to LDS buffer
+//   (c+1) % 2, barrier (LDS only).
+// Loads are issued in the order they are waited for, so the wait before each
+// LDS write leaves the younger code prefetches in flight.  The activation
+// tile is XOR-swizzled by row in LDS (conflict-free 16-byte writes and
+// fragment reads; the Petit blog, "Mastering the memory hierarchy").
 template <int FMT, int WM, int WN, int MBW, int TNW, bool KTAIL>
-__global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A, const u32x4* __restrict__ wq,
-                                                 const uint8_t* __restrict__ sq, uint16_t* __restrict__ C, int M,
-                                                 int N, int K, int KB, int SB, int NT) {
+__global__ __launch_bounds__(256) void gemm_prefill(const uint16_t* __restrict__ A, const u32x4* __restrict__ wq,
+                                                   const uint8_t* __restrict__ sq, uint16_t* __restrict__ C,
+                                                   float* __restrict__ P, int M, int N, int K, int KB, int SB, int NT,
+                                                   int S) {
     static_assert(WM * WN == 4, "four waves");
+    typedef u32x4 SW;
     constexpr int BM = WM * MBW * 16;  // m rows per workgroup
     constexpr int BNT = WN * TNW;      // n-tiles per workgroup
     constexpr int kBuf = BM * 256;     // one LDS activation buffer (BM x 128 K x 2 B)
     constexpr int kStage = BM / 16;    // 16-byte activation pieces per thread per chunk
+    constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kBuf];
 
     const int tid = threadIdx.x;
@@ -435,17 +437,21 @@ __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A
     const int r = lane & 15, j = lane >> 4;
     const int wm = wave % WM, wn = wave / WM;
 
-    // XCD-banded work order
+    // work item: K split ks (innermost), then an XCD-banded (m-tile, n-group) order
     const int MT = (M + BM - 1) / BM, NG = (NT + BNT - 1) / BNT;
+    const int ks = blockIdx.x % S;
+    const int item = blockIdx.x / S;
     const int total = MT * NG;
-    int L = blockIdx.x;
-    if (total % kXcdCount == 0) L = (blockIdx.x % kXcdCount) * (total / kXcdCount) + blockIdx.x / kXcdCount;
+    int L = item;
+    if (total % kXcdCount == 0 && S == 1)
+        L = (item % kXcdCount) * (total / kXcdCount) + item / kXcdCount;
     const int mt = L % MT, ng = L / MT;
     const int m0 = mt * BM;
     const int tile0 = ng * BNT + wn * TNW;
+    const int sb0 = (ks * SB) / S, sb1 = ((ks + 1) * SB) / S;
+    const int c0 = 4 * sb0, clast = 4 * sb1 - 1;
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(M * K * 2));
-    constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();
     const int soff = scale_lane_offset<FMT>(r, j);
     __amdgpu_buffer_rsrc_t rw[TNW], rs[TNW];
 #pragma unroll
@@ -465,18 +471,29 @@ __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A
         aoff[q] = (uint32_t)((m0 + row) * K + col * 8) * 2u;
         lds_off[q] = row * 256 + ((col ^ (row & 15)) << 4);
     }
-    auto load_stage = [&](int b, u32x4 (&st)[kStage]) {
+    u32x4 st[2][kStage];
+    auto a_issue = [&](auto set_c, int chunk) {
+        constexpr int SET = decltype(set_c)::value;
+        chunk = min(chunk, clast);
 #pragma unroll
         for (int q = 0; q < kStage; ++q) {
-            const int col = ((tid + 256 * q) & 15);
-            const int k = b * kChunkK + col * 8;
-            const uint32_t off = aoff[q] + (uint32_t)(b * kChunkK) * 2u;
-            st[q] = load_a(ra, (!KTAIL || k < K) ? off : kOutOfRange);
+            const int k = chunk * kChunkK + (((tid + 256 * q) & 15) * 8);
+            const uint32_t off = aoff[q] + (uint32_t)(chunk * kChunkK) * 2u;
+            st[SET][q] = load_a(ra, (!KTAIL || k < K) ? off : kOutOfRange);
         }
     };
-    auto store_stage = [&](int buf, const u32x4 (&st)[kStage]) {
+    auto a_store = [&](auto set_c) {
+        constexpr int SET = decltype(set_c)::value;
 #pragma unroll
-        for (int q = 0; q < kStage; ++q) *reinterpret_cast<u32x4*>(lds_a + buf * kBuf + lds_off[q]) = st[q];
+        for (int q = 0; q < kStage; ++q) *reinterpret_cast<u32x4*>(lds_a + SET * kBuf + lds_off[q]) = st[SET][q];
+    };
+    u32x4 wr[4][TNW];
+    auto w_issue = [&](auto slot_c, int chunk) {
+        constexpr int SL = decltype(slot_c)::value;
+        chunk = min(chunk, clast);
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt)
+            wr[SL][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, kLoadStream);
     };
     auto lds_barrier = [] {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -490,10 +507,14 @@ __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // multiply chunk b (activations in LDS buffer buf) with code blocks w
-    auto compute = [&](auto cc, int buf, const u32x4 (&w)[TNW], const u32x4 (&sc)[TNW]) {
-        constexpr int CC = decltype(cc)::value;
-        const uint8_t* base = lds_a + buf * kBuf;
+    // multiply chunk (position T in its 512-K block) from LDS buffer BUF.
+    // The dequant of tile tt+1 is placed before the products of tile tt and
+    // the scheduler is asked to alternate one matrix instruction with two
+    // vector instructions, so the dequant runs while the matrix core works.
+    auto compute = [&](auto t_c, auto buf_c, const SW (&sc)[TNW]) {
+        constexpr int T = decltype(t_c)::value;
+        constexpr int BUF = decltype(buf_c)::value;
+        const uint8_t* base = lds_a + BUF * kBuf;
         auto step = [&](auto ii) {
             constexpr int I = decltype(ii)::value;
             u32x4 a[MBW];
@@ -503,11 +524,19 @@ __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A
                 const int col = 4 * I + j;
                 a[mb] = *reinterpret_cast<const u32x4*>(base + row * 256 + ((col ^ (row & 15)) << 4));
             }
+            u32x4 wf[TNW];
+            wf[0] = dequant_step<FMT, T, I>(wr[T][0], sc[0]);
 #pragma unroll
             for (int tt = 0; tt < TNW; ++tt) {
-                const u32x4 wf = dequant_step<FMT, CC, I>(w[tt], sc[tt]);
+                if (tt + 1 < TNW) wf[tt + 1] = dequant_step<FMT, T, I>(wr[T][tt + 1], sc[tt + 1]);
 #pragma unroll
-                for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = mfma_bf16(wf, a[mb], acc[tt][mb]);
+                for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = mfma_bf16(wf[tt], a[mb], acc[tt][mb]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, MBW, 0);  // fragment reads first
+#pragma unroll
+            for (int q = 0; q < MBW * TNW; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
             }
         };
         step(std::integral_constant<int, 0>{});
@@ -515,47 +544,62 @@ __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A
         step(std::integral_constant<int, 2>{});
         step(std::integral_constant<int, 3>{});
     };
+    // step for chunk c = base + T (T = c % 4; c % 2 == T % 2)
+    auto pstep = [&](auto t_c, int base, const SW (&cur)[TNW]) {
+        constexpr int T = decltype(t_c)::value;
+        a_issue(std::integral_constant<int, T % 2>{}, base + T + 2);
+        w_issue(std::integral_constant<int, (T + 3) % 4>{}, base + T + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t_c, std::integral_constant<int, T % 2>{}, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        a_store(std::integral_constant<int, (T + 1) % 2>{});
+        lds_barrier();
+    };
+    SW sa[TNW], sbs[TNW];
+    auto block = [&](int sbx, const SW (&cur)[TNW], SW (&nxt)[TNW]) {
+        const int base = 4 * sbx;
+        const int nsb = min(sbx + 1, sb1 - 1);
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt) nxt[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
+        pstep(std::integral_constant<int, 0>{}, base, cur);
+        pstep(std::integral_constant<int, 1>{}, base, cur);
+        pstep(std::integral_constant<int, 2>{}, base, cur);
+        pstep(std::integral_constant<int, 3>{}, base, cur);
+    };
 
-    const int last = KB - 1;
-    u32x4 st[kStage];
-    u32x4 w0[TNW], w1[TNW], sc[TNW], scn[TNW];
-    load_stage(0, st);
 #pragma unroll
-    for (int tt = 0; tt < TNW; ++tt) {
-        w0[tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, 0, 0);
-        sc[tt] = load_scale_block<FMT>(rs[tt], soff, 0);
-    }
-    store_stage(0, st);
+    for (int tt = 0; tt < TNW; ++tt) sa[tt] = load_scale_block<FMT>(rs[tt], soff, sb0);
+    a_issue(std::integral_constant<int, 0>{}, c0);
+    w_issue(std::integral_constant<int, 0>{}, c0);
+    w_issue(std::integral_constant<int, 1>{}, c0 + 1);
+    w_issue(std::integral_constant<int, 2>{}, c0 + 2);
+    a_issue(std::integral_constant<int, 1>{}, c0 + 1);
+    a_store(std::integral_constant<int, 0>{});
     lds_barrier();
-    // chunk pairs (b even in w0, b odd in w1); a scale block is 4 chunks
-    for (int sb = 0; sb < SB; ++sb) {
-        const int nsb = min(sb + 1, SB - 1);
-        auto half = [&](auto cc, const u32x4 (&wc)[TNW], u32x4 (&wn)[TNW]) {
-            constexpr int CC = decltype(cc)::value;
-            const int b = 4 * sb + CC;
-            const int bn = min(b + 1, last);
-            load_stage(bn, st);
-#pragma unroll
-            for (int tt = 0; tt < TNW; ++tt) {
-                wn[tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, bn * 1024, 0);
-                if constexpr (CC == 3) scn[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
-            }
-            compute(cc, b & 1, wc, sc);
-            store_stage((b + 1) & 1, st);
-            lds_barrier();
-        };
-        half(std::integral_constant<int, 0>{}, w0, w1);
-        half(std::integral_constant<int, 1>{}, w1, w0);
-        half(std::integral_constant<int, 2>{}, w0, w1);
-        half(std::integral_constant<int, 3>{}, w1, w0);
-#pragma unroll
-        for (int tt = 0; tt < TNW; ++tt) sc[tt] = scn[tt];
+    int sb = sb0;
+    for (; sb + 1 < sb1; sb += 2) {
+        block(sb, sa, sbs);
+        block(sb + 1, sbs, sa);
     }
+    if (sb < sb1) block(sb, sa, sbs);
+
 #pragma unroll
     for (int tt = 0; tt < TNW; ++tt)
 #pragma unroll
-        for (int mb = 0; mb < MBW; ++mb)
-            store_frag(C, acc[tt][mb], m0 + wm * MBW * 16 + mb * 16 + r, (tile0 + tt) * kTileN + 4 * j, M, N);
+        for (int mb = 0; mb < MBW; ++mb) {
+            const int m = m0 + wm * MBW * 16 + mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
+            if (P == nullptr) {
+                store_frag(C, acc[tt][mb], m, n0, M, N);
+            } else if (m < M) {
+                float* dst = P + ((size_t)ks * M + m) * N + n0;
+                if ((N & 3) == 0 && n0 + 3 < N) {
+                    *reinterpret_cast<f32x4*>(dst) = acc[tt][mb];
+                } else {
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + e < N) dst[e] = acc[tt][mb][e];
+                }
+            }
+        }
 }
 
 // ------------------------------------------------------------ debug dequant
@@ -615,7 +659,7 @@ static int64_t a_row_block(int64_t M) {
     if (M <= 16) return 16;
     if (M <= 32) return 32;
     if (M <= 64) return 64;
-    return 256;  // largest tiled m-block
+    return 128;  // prefill m-block
 }
 
 // Decode-kernel shape: TN n-tiles per wave, NWN waves per K group, NWK K
@@ -758,52 +802,77 @@ static void launch_reduce(const float* P, uint16_t* C, int64_t total, int S, hip
     reduce_partials<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(P, C, total, S);
 }
 
-// Tiled-kernel shape: WM x WN waves, MBW m-blocks and TNW n-tiles per wave.
-struct TiledShape {
-    int wm, wn, mbw, tnw;
+// Prefill-kernel shape: WM x WN waves, MBW m-blocks and TNW n-tiles per wave,
+// K split over S workgroups.
+struct PrefillShape {
+    int wm, wn, mbw, tnw, s;
 };
 
-static TiledShape tiled_override() {
-    static const TiledShape ov = [] {
-        TiledShape t{0, 0, 0, 0};
-        const char* e = getenv("FP4GEMM_TILED");
-        if (e) sscanf(e, "%d,%d,%d,%d", &t.wm, &t.wn, &t.mbw, &t.tnw);
+static PrefillShape prefill_override() {
+    static const PrefillShape ov = [] {
+        PrefillShape t{0, 0, 0, 0, 1};
+        const char* e = getenv("FP4GEMM_PREFILL");
+        if (e) sscanf(e, "%d,%d,%d,%d,%d", &t.wm, &t.wn, &t.mbw, &t.tnw, &t.s);
         return t;
     }();
     return ov;
 }
 
+// Compiled prefill shapes: X(WM, WN, MBW, TNW).
+#define FP4_PREFILL_SHAPES(X) \
+    X(1, 4, 8, 2) X(1, 4, 8, 4) X(2, 2, 4, 4) X(2, 2, 4, 2) X(1, 4, 8, 1) X(2, 2, 4, 1) X(1, 4, 4, 4)
+
+static bool prefill_compiled(const PrefillShape& t) {
+#define FP4_PREFILL_HAS(WM_, WN_, MBW_, TNW_) \
+    if (t.wm == WM_ && t.wn == WN_ && t.mbw == MBW_ && t.tnw == TNW_) return true;
+    FP4_PREFILL_SHAPES(FP4_PREFILL_HAS)
+#undef FP4_PREFILL_HAS
+    return false;
+}
+
 // Measured on MI355X over the Llama-3-70B prefill shapes (m = 256): one wave
-// over all 128 rows of the block amortizes each dequantized code over 128
-// products; wide-N shapes take two n-tiles per wave.
-static TiledShape pick_tiled(int M, int NT) {
-    (void)M;
-    TiledShape ov = tiled_override();
-    if (ov.wm > 0) return ov;
-    return NT >= 640 ? TiledShape{1, 4, 8, 2} : TiledShape{1, 4, 8, 1};
+// over all 128 rows of the block with four n-tiles amortizes each
+// dequantized fragment over 8 products and each activation fragment read
+// from LDS over 4; K is split until about 160 workgroups run (QKV 2, O and
+// down 4, gate_up 1).  FP4GEMM_PREFILL="WM,WN,MBW,TNW,S" overrides it.
+static PrefillShape pick_prefill(int fmt, int64_t M, int64_t N, int NT, int SB) {
+    (void)fmt;
+    (void)N;
+    PrefillShape t = prefill_override();
+    if (t.wm > 0 && prefill_compiled(t)) {
+        t.s = t.s < 1 ? 1 : (t.s > SB ? SB : t.s);
+        return t;
+    }
+    t = PrefillShape{1, 4, 8, 4, 1};
+    const int64_t blocks = ((M + 127) / 128) * ((NT + 15) / 16);
+    while (blocks * t.s < 160 && t.s < 8 && 2 * t.s <= SB) t.s *= 2;
+    return t;
 }
 
 template <int FMT, int WM, int WN, int MBW, int TNW>
-static void launch_tiled_t(const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, int M, int N, int K,
-                           int KB, int SB, int NT, hipStream_t s) {
+static void launch_prefill_t(int S, const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, float* P,
+                             int M, int N, int K, int KB, int SB, int NT, hipStream_t s) {
     constexpr int BM = WM * MBW * 16, BNT = WN * TNW;
-    const int grid = ((M + BM - 1) / BM) * ((NT + BNT - 1) / BNT);
+    const int grid = ((M + BM - 1) / BM) * ((NT + BNT - 1) / BNT) * S;
     if (K % kScaleBlockK == 0)
-        gemm_tiled<FMT, WM, WN, MBW, TNW, false><<<dim3(grid), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+        gemm_prefill<FMT, WM, WN, MBW, TNW, false><<<dim3(grid), dim3(256), 0, s>>>(A, wq, sq, C, P, M, N, K, KB, SB,
+                                                                                   NT, S);
     else
-        gemm_tiled<FMT, WM, WN, MBW, TNW, true><<<dim3(grid), dim3(256), 0, s>>>(A, wq, sq, C, M, N, K, KB, SB, NT);
+        gemm_prefill<FMT, WM, WN, MBW, TNW, true><<<dim3(grid), dim3(256), 0, s>>>(A, wq, sq, C, P, M, N, K, KB, SB,
+                                                                                  NT, S);
 }
 
 template <int FMT>
-static void launch_tiled(TiledShape t, const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C, int M,
-                         int N, int K, int KB, int SB, int NT, hipStream_t s) {
-#define FP4_TILED_CASE(WM_, WN_, MBW_, TNW_)                                                         \
-    if (t.wm == WM_ && t.wn == WN_ && t.mbw == MBW_ && t.tnw == TNW_)                                \
-        return launch_tiled_t<FMT, WM_, WN_, MBW_, TNW_>(A, wq, sq, C, M, N, K, KB, SB, NT, s);
-    FP4_TILED_CASE(1, 4, 8, 1) FP4_TILED_CASE(1, 4, 8, 2) FP4_TILED_CASE(1, 4, 4, 1) FP4_TILED_CASE(1, 4, 4, 2)
-    FP4_TILED_CASE(2, 2, 4, 4) FP4_TILED_CASE(2, 2, 4, 2)
-#undef FP4_TILED_CASE
-    launch_tiled_t<FMT, 1, 4, 8, 1>(A, wq, sq, C, M, N, K, KB, SB, NT, s);  // shape not compiled: default
+static bool launch_prefill(const PrefillShape& t, const uint16_t* A, const u32x4* wq, const uint8_t* sq, uint16_t* C,
+                           float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s) {
+#define FP4_PREFILL_CASE(WM_, WN_, MBW_, TNW_)                                                         \
+    if (t.wm == WM_ && t.wn == WN_ && t.mbw == MBW_ && t.tnw == TNW_) {                                \
+        launch_prefill_t<FMT, WM_, WN_, MBW_, TNW_>(t.s, A, wq, sq, C, P, M, N, K, KB, SB, NT, s);     \
+        return true;                                                                                   \
+    }
+    FP4_PREFILL_SHAPES(FP4_PREFILL_CASE)
+#undef FP4_PREFILL_CASE
+    return false;
 }
 
 template <int FMT>
@@ -817,15 +886,22 @@ static int launch_gemm(const uint16_t* A, const u32x4* wq, const uint8_t* sq, ui
         if (P) launch_reduce(P, C, (int64_t)M * N, d.s, s);
         return FP4_OK;
     }
-    launch_tiled<FMT>(pick_tiled(M, NT), A, wq, sq, C, M, N, K, KB, SB, NT, s);
+    const PrefillShape t = pick_prefill(FMT, M, N, NT, SB);
+    float* P = t.s > 1 ? static_cast<float*>(ws) : nullptr;
+    if (!launch_prefill<FMT>(t, A, wq, sq, C, P, M, N, K, KB, SB, NT, s)) return FP4_ERR_SHAPE;
+    if (P) launch_reduce(P, C, (int64_t)M * N, t.s, s);
     return FP4_OK;
 }
 
 // Workspace bytes of the kernel fp4_gemm picks for this problem.
 static size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
-    if (M == 0 || M > 64) return 0;
-    const int MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    if (M == 0) return 0;
     const int SB = int(padded_k(K) / kScaleBlockK), NT = int(padded_n(N) / kTileN);
+    if (M > 64) {
+        const PrefillShape t = pick_prefill(fmt, M, N, NT, SB);
+        return t.s > 1 ? (size_t)t.s * (size_t)M * (size_t)N * sizeof(float) : 0;
+    }
+    const int MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     return decode_workspace_bytes(pick_decode(fmt, MB, M, N, NT, SB), M, N);
 }
 

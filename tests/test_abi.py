@@ -185,15 +185,20 @@ def test_workspace_size_is_a_split_k_partial_buffer():
     # 0 (no K split) or S * m * N * 4 bytes with 2 <= S <= 16 and S <= K / 512,
     # a pure function of the arguments.
     for m, N, K, fmt in ((16, 8192, 8192, 0), (16, 57344, 8192, 0), (16, 8192, 28672, 0), (1, 8192, 28672, 1),
-                         (33, 100, 544, 1), (64, 10240, 8192, 0), (7, 1000, 8192, 0)):
+                         (33, 100, 544, 1), (64, 10240, 8192, 0), (7, 1000, 8192, 0), (256, 8192, 8192, 0),
+                         (300, 96, 640, 0)):
         b = F.workspace_size(m, N, K, fmt)
         assert b == F.workspace_size(m, N, K, fmt)
         if b:
             S, rem = divmod(b, 4 * m * N)
             assert rem == 0 and 2 <= S <= min(16, -(-K // 512)), (m, N, K, b)
-    for m in (0, 65, 256, 1000):
-        assert F.workspace_size(m, 8192, 8192, 0) == 0
-    assert F.new_workspace(256, 8192, 8192, 0) is None
+    assert F.workspace_size(0, 8192, 8192, 0) == 0
+    # prefill m: split only while fewer than ~160 workgroups would run
+    for m, N, K in ((256, 8192, 8192), (256, 10240, 8192), (256, 8192, 28672), (65, 1000, 8192)):
+        b = F.workspace_size(m, N, K, 0)
+        assert b % (4 * m * N) == 0 and b // (4 * m * N) in (0, 2, 4, 8)
+    assert F.workspace_size(256, 57344, 8192, 0) == 0
+    assert F.new_workspace(1000, 57344, 8192, 0) is None
 
 
 def test_gemm_rejects_small_or_misaligned_workspace_before_any_hip_call():

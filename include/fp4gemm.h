@@ -1,9 +1,9 @@
 /*
- * fp4gemm.h -- C ABI of the BF16 x FP4 block-scaled GEMM for AMD MI355X (gfx950).
+ * fp4gemm.h -- C ABI of the BF16 / FP16 x FP4 block-scaled GEMM for AMD MI355X (gfx950).
  *
  *   Y[m][N] = A[m][K] . dequant(W)[N][K]^T,   dequant(W)[n][k] = e2m1(code[n][k]) * scale[n][k / G]
  *
- * A and Y are BF16, accumulation is FP32.  W is stored as FP4 E2M1 codes with
+ * A and Y are BF16 (fp4_gemm) or FP16 (fp4_gemm_f16), accumulation is FP32.  W is stored as FP4 E2M1 codes with
  * one scale per G consecutive K-elements of a row:
  *   NVFP4: G = 16, scale = FP8 E4M3 (OCP "E4M3FN")  -- Petit blog ("Optimizing
  *          FP4 Mixed-Precision Inference on AMD GPUs"), section "Detailed
@@ -128,12 +128,29 @@ int fp4_gemm(const void* A, const void* wq, const void* sq, void* C,
              int64_t m, int64_t N, int64_t K, int format,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Same as fp4_gemm with FP16 activations and output: A device FP16 [m][K],
+ * C device FP16 [m][N] (the Petit blog, "Introduction": FP16/BF16 x FP4
+ * kernels).  The weights use the same packed layout; they are dequantized
+ * to FP16 (exact for every NVFP4 code x scale product, and for MXFP4 scale
+ * exponents -23 .. 13; outside that range products round or overflow in
+ * FP16).  Accumulation FP32, output rounded to FP16 to nearest even.
+ * Workspace, alignment, errors and determinism as for fp4_gemm (the
+ * workspace size is the same). */
+int fp4_gemm_f16(const void* A, const void* wq, const void* sq, void* C,
+                 int64_t m, int64_t N, int64_t K, int format,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Debug/test entry: write dequant(W) as BF16 [N][K] row-major to device
  * memory W_bf16 with the same device dequantization the GEMM uses (the
  * per-block debug dump suggested by the mhpq.cn article, section 7).
  * Every code x scale product is exact in BF16 for valid scales. */
 int fp4_dequant(const void* wq, const void* sq, void* W_bf16, int64_t N, int64_t K, int format,
                 void* stream);
+
+/* As fp4_dequant, writing FP16 [N][K] with the dequantization fp4_gemm_f16
+ * uses. */
+int fp4_dequant_f16(const void* wq, const void* sq, void* W_f16, int64_t N, int64_t K, int format,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,45 @@
+// Host-side launch interface between the C ABI (fp4gemm.hip) and the kernel
+// instantiations, one translation unit per kernel family and activation type
+// (decode_bf16.hip, decode_f16.hip, prefill_bf16.hip, prefill_f16.hip), which
+// are compiled in parallel.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+// Decode kernel: TN n-tiles per wave, NWN waves per K group, NWK K groups per
+// workgroup, K split over S workgroups.
+struct DecodeShape {
+    int tn, nwn, nwk, s;
+};
+
+// Prefill kernel: WM x WN waves, MBW m-blocks and TNW n-tiles per wave, K split
+// over S workgroups.
+struct PrefillShape {
+    int wm, wn, mbw, tnw, s;
+};
+
+// Compiled decode shapes: X(MB, TN, NWN, NWK).
+#define FP4_DECODE_SHAPES(X)                                                                         \
+    X(1, 1, 4, 1) X(1, 2, 4, 1) X(1, 1, 4, 2) X(1, 2, 4, 2) X(1, 1, 4, 4) X(1, 2, 1, 4) X(1, 2, 1, 1)  \
+    X(1, 2, 7, 1) X(1, 1, 7, 1) X(1, 2, 7, 2) X(1, 2, 5, 1) X(1, 1, 5, 2) X(1, 1, 8, 1) X(1, 2, 8, 1)  \
+    X(1, 1, 8, 2) X(2, 1, 4, 1) X(2, 1, 4, 2) X(2, 1, 8, 1) X(2, 2, 4, 1) X(4, 1, 4, 1) X(4, 1, 8, 1)  \
+    X(4, 2, 4, 1)
+
+// Compiled prefill shapes: X(WM, WN, MBW, TNW).
+#define FP4_PREFILL_SHAPES(X) \
+    X(1, 4, 8, 2) X(1, 4, 8, 4) X(2, 2, 4, 4) X(2, 2, 4, 2) X(1, 4, 8, 1) X(2, 2, 4, 1) X(1, 4, 4, 4)
+
+// Launch one GEMM kernel on stream s (P: FP32 partials of a K split, else
+// null).  False when the shape is not compiled.
+bool launch_decode_bf16(int fmt, int MB, const DecodeShape& d, const void* A, const void* wq, const void* sq,
+                        void* C, float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s);
+bool launch_decode_f16(int fmt, int MB, const DecodeShape& d, const void* A, const void* wq, const void* sq, void* C,
+                       float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s);
+bool launch_prefill_bf16(int fmt, const PrefillShape& t, const void* A, const void* wq, const void* sq, void* C,
+                         float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s);
+bool launch_prefill_f16(int fmt, const PrefillShape& t, const void* A, const void* wq, const void* sq, void* C,
+                        float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s);
+
+}  // namespace fp4

@@ -1,0 +1,686 @@
+// BF16 / FP16 x FP4 (NVFP4 / MXFP4) GEMM kernels for gfx950 (device code).
+//
+//   Y[m][N] = A[m][K] . dequant(W)[N][K]^T, FP32 accumulation, output in the
+//   activation type (ACT = 0: BF16, ACT = 1: FP16).
+//
+// Design (MI355X-first; the Petit blog "Optimizing FP4 Mixed-Precision
+// Inference on AMD GPUs" is prior art written for MI300):
+//  * Weights stay FP4 in HBM and are dequantized in registers to BF16 right
+//    before the BF16 matrix-core instruction (the blog's section "Efficient
+//    dequantization through preprocessing": no native FP4 x BF16 matrix core,
+//    so FP4 -> BF16 in registers, then BF16 MFMA).  Activations are never
+//    re-quantized.
+//  * The weight layout is pre-arranged offline (layout.h) so that each lane
+//    loads its MFMA fragment straight from HBM into VGPRs with one 16-byte
+//    load and a wave reads one contiguous 1 KiB block.
+//  * Activations are read with ranged buffer loads: rows >= m and K-padding
+//    read as zero without branches (the blog's section "Generating
+//    high-quality machine code": ranged buffer loads drop out-of-bounds
+//    accesses).
+//  * The activation tile of the large-m kernel is staged in LDS with an XOR
+//    swizzle so that both the 16-byte writes and the fragment reads are free
+//    of bank conflicts (the blog's section "Mastering the memory hierarchy").
+//  * Dequant: gfx950 v_cvt_scalef32_pk_{f32,bf16}_fp4 converts two E2M1 codes
+//    per instruction.  Its scale operand only contributes its exponent
+//    (checked on the device), which is exactly an E8M0 scale, so MXFP4 is
+//    one instruction per two weights.  E4M3 scales carry mantissa bits, so
+//    NVFP4 converts exactly to FP32, multiplies by the decoded scale (exact:
+//    at most 6 significant bits) and keeps the upper halves (exact BF16).
+//    FP16 activations (the Petit blog, "Introduction": FP16/BF16 x FP4): the
+//    FP4 -> FP16 convert applies the scale's exponent and one packed FP16
+//    multiply applies its mantissa, both exact.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
+
+#include "../../include/fp4gemm.h"
+#include "layout.h"
+
+namespace fp4 {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer resource word 3 for raw (stride 0) 32-bit buffer access on gfx9-family
+// parts; an offset at or past the buffer's byte range reads zero.
+constexpr int kBufWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache-policy operand of buffer loads that stream data read once (the
+// weight codes and scales): the nontemporal hint.
+constexpr int kLoadStream = 2;
+constexpr int kXcdCount = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// ------------------------------------------------------------------ dequant
+// Keep the upper 16 bits of two FP32 values (exact when both are BF16 values).
+__device__ __forceinline__ uint32_t upper_halves(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// NVFP4: eight codes (low nibble of byte 0 first) times FP32 scale s -> eight
+// BF16 values in K order, packed two per dword.
+__device__ __forceinline__ u32x4 dequant_nvfp4(uint32_t w, float s) {
+    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    u32x4 o;
+    o.x = upper_halves(f0.x * s, f0.y * s);
+    o.y = upper_halves(f1.x * s, f1.y * s);
+    o.z = upper_halves(f2.x * s, f2.y * s);
+    o.w = upper_halves(f3.x * s, f3.y * s);
+    return o;
+}
+
+// MXFP4: the scale operand is an FP32 whose exponent field is the E8M0 byte.
+__device__ __forceinline__ u32x4 dequant_mxfp4(uint32_t w, float sexp) {
+    u32x4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sexp, 0));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sexp, 1));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sexp, 2));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sexp, 3));
+    return o;
+}
+
+// Scales of one lane for one 512-K scale block: 16 bytes; byte 4 c + i is the
+// scale of MFMA step i of chunk c (layout.h).  Lane byte offset inside the
+// block: NVFP4 (j / 2) * 256 + r * 16, MXFP4 r * 16.
+template <int FMT>
+__device__ __forceinline__ int scale_lane_offset(int r, int j) {
+    return FMT == 0 ? (j >> 1) * 256 + r * 16 : r * 16;
+}
+template <int FMT>
+constexpr int scale_block_bytes() { return FMT == 0 ? 512 : 256; }
+
+// FP16 targets.  NVFP4: the convert's scale operand is the decoded E4M3
+// scale s, of which it applies the exponent (c x 2^e, exact in FP16: between
+// 2^-10 and 1536); the packed multiply applies s / 2^e in [1, 2) (at most 4
+// significant bits; the product has at most 6: exact).  A zero scale gives
+// c x 2^-127, which rounds to zero in FP16.  MXFP4: the E8M0 scale is the
+// convert's scale operand; exact for exponents -23 .. 13.
+__device__ __forceinline__ u32x4 dequant_nvfp4_f16(uint32_t w, float s) {
+    const uint32_t mant = 0x3C00u | ((__float_as_uint(s) >> 13) & 0x3FFu);  // FP16 bits of s / 2^e
+    const f16x2 m2 = __builtin_bit_cast(f16x2, mant | (mant << 16));
+    u32x4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 0) * m2);
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 1) * m2);
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2) * m2);
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3) * m2);
+    return o;
+}
+
+__device__ __forceinline__ u32x4 dequant_mxfp4_f16(uint32_t w, float sexp) {
+    u32x4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sexp, 0));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sexp, 1));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sexp, 2));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sexp, 3));
+    return o;
+}
+
+// Dequantize MFMA step I (dword I of the lane's 16 bytes) of chunk C into the
+// activation type ACT.  NVFP4: OCP E4M3 -> FP32 with the hardware FP8
+// convert (OCP encoding on gfx950, checked on the device).  MXFP4: the E8M0
+// byte becomes the exponent field of the FP32 scale operand.
+template <int FMT, int C, int I, int ACT = 0>
+__device__ __forceinline__ u32x4 dequant_step(const u32x4& w, const u32x4& s) {
+    if constexpr (FMT == 0) {
+        const float sf = __builtin_amdgcn_cvt_f32_fp8((int)s[C], I);
+        if constexpr (ACT == 0) return dequant_nvfp4(w[I], sf);
+        else return dequant_nvfp4_f16(w[I], sf);
+    } else {
+        const float se = __uint_as_float(((s[C] >> (8 * I)) & 0xFFu) << 23);
+        if constexpr (ACT == 0) return dequant_mxfp4(w[I], se);
+        else return dequant_mxfp4_f16(w[I], se);
+    }
+}
+
+// 16x16x32 matrix-core product in the activation type, FP32 accumulate.
+template <int ACT = 0>
+__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
+    if constexpr (ACT == 0)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load_a(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Two FP32 values rounded to nearest even into the output type, packed.
+template <int ACT = 0>
+__device__ __forceinline__ uint32_t pack_out(float lo, float hi) {
+    if constexpr (ACT == 0) {
+        bf16x2 v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        f16x2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+// Store one 16x16 output fragment: lane holds Y[m][n0 .. n0+3] (MFMA output
+// rows are n, columns are m).
+template <int ACT = 0>
+__device__ __forceinline__ void store_frag(uint16_t* __restrict__ C, const f32x4& v, int m, int n0, int M, int N) {
+    if (m >= M) return;
+    const uint32_t p0 = pack_out<ACT>(v.x, v.y), p1 = pack_out<ACT>(v.z, v.w);
+    uint16_t* dst = C + (size_t)m * N + n0;
+    if ((N & 3) == 0 && n0 + 3 < N) {
+        u32x2 pv = {p0, p1};
+        *reinterpret_cast<u32x2*>(dst) = pv;
+    } else {
+        const uint16_t h[4] = {(uint16_t)(p0 & 0xFFFF), (uint16_t)(p0 >> 16), (uint16_t)(p1 & 0xFFFF),
+                               (uint16_t)(p1 >> 16)};
+        for (int e = 0; e < 4; ++e)
+            if (n0 + e < N) dst[e] = h[e];
+    }
+}
+
+// ------------------------------------------------------------ buffer loads
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufWord3);
+}
+
+template <int FMT>
+__device__ __forceinline__ u32x4 load_scale_block(__amdgpu_buffer_rsrc_t r, int soff_lane, int sb) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, soff_lane, sb * scale_block_bytes<FMT>(), kLoadStream);
+}
+
+// ------------------------------------------------------------ decode GEMM
+// Small m (<= 16*MB) with the activations shared through LDS.  A workgroup has
+// NWK groups of NWN waves.  The waves of one group cover the same K range and
+// different n-tiles (TN each), so one activation chunk in LDS feeds
+// TN*NWN tiles: each activation byte crosses the L1/L2 path once per
+// workgroup instead of once per wave, and the loads that bring it in read
+// whole 128-byte lines (8 rows x 128 bytes per wave instruction).  The NWK
+// groups split the workgroup's K range and are summed through LDS in a fixed
+// order.  Narrow layers also split K over S workgroups: each writes FP32
+// partial sums to the caller's workspace and reduce_partials adds them in a
+// fixed order (no atomics, deterministic).
+//
+// Pipeline.  Code blocks stream through a four-slot register ring, three
+// 128-K chunks ahead of the multiply.  Activations move one 512-K scale block
+// at a time through two LDS buffers: at the start of block x the
+// activations of block x+1 are issued into registers (before the code blocks
+// issued during block x, so waiting for them never waits for a younger code
+// prefetch), and at the end of block x they are written to the buffer block
+// x-1 used.  One barrier per block (LDS only: the prefetches stay in flight)
+// separates those writes from the reads of block x+1 and the reads of block
+// x-1 from the writes.
+template <int FMT, int ACT, int MB, int TN, int NWN, int NWK>
+__global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __restrict__ A,
+                                                             const u32x4* __restrict__ wq,
+                                                             const uint8_t* __restrict__ sq,
+                                                             uint16_t* __restrict__ C, float* __restrict__ P, int M,
+                                                             int N, int K, int KB, int SB, int NT, int S) {
+    typedef u32x4 SW;
+    constexpr int kRows = 16 * MB;  // activation rows; one 1 KiB load per row per block
+    // Activation load instructions per wave per block.  When NWN does not
+    // divide the row count, the surplus loads repeat the last row: they
+    // write the same bytes to the same LDS slot as its first load.
+    constexpr int QB = (kRows + NWN - 1) / NWN;
+    constexpr int kBuf = MB * 4096;  // one chunk: 16*MB rows x 128 K x 2 B
+    constexpr int kBlk = 4 * kBuf;     // one 512-K block
+    constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[NWK * 2 * kBlk];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % NWN, wk = wave / NWN;
+    const int r = lane & 15, j = lane >> 4;
+    const int ks = blockIdx.x % S, grp = blockIdx.x / S;
+    const int tile0 = grp * (TN * NWN) + wn * TN;
+    const int soff = scale_lane_offset<FMT>(r, j);
+
+    // K range of the workgroup and of this wave's group, in 512-K scale blocks.
+    // Every group runs nblk blocks so that all waves meet at every barrier; a
+    // group with fewer blocks skips the multiply of the extra ones.
+    const int wsb0 = (ks * SB) / S, wsb1 = ((ks + 1) * SB) / S;
+    const int span = wsb1 - wsb0;
+    const int sb0 = wsb0 + (wk * span) / NWK, sb1 = wsb0 + ((wk + 1) * span) / NWK;
+    const int nblk = (span + NWK - 1) / NWK;
+    const int own = sb1 - sb0;
+    const int sbmax = own > 0 ? sb1 - 1 : wsb0;         // last block this group may read
+    const int cmax = own > 0 ? 4 * sb1 - 1 : 4 * wsb0;  // last chunk this group may read
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(M * K * 2));
+    __amdgpu_buffer_rsrc_t rw[TN], rs[TN];
+#pragma unroll
+    for (int tt = 0; tt < TN; ++tt) {
+        const int t = min(tile0 + tt, NT - 1);
+        rw[tt] = make_rsrc(reinterpret_cast<const uint8_t*>(wq) + (size_t)t * KB * 1024, (uint32_t)KB * 1024u);
+        rs[tt] = make_rsrc(sq + (size_t)t * SB * kScaleBlockBytes, (uint32_t)(SB * kScaleBlockBytes));
+    }
+
+    // Activations in LDS, per 128-K chunk: the 16-byte fragment of MFMA step
+    // I, m-block mb, lane (j, r) sits in slot 16 j + (r ^ (4 I + j)) of the
+    // 1 KiB run (I, mb).  The XOR spreads the 16 octets of one row over all
+    // 16 bank groups, so the row-contiguous writes below and the fragment
+    // reads are both free of bank conflicts.
+    // Load u of this wave brings row q = wn + NWN u of a 512-K block: lane l
+    // reads the 16 contiguous bytes at k = 512 sb + 8 l (chunk l / 16, octet
+    // l % 16), so one instruction is 1 KiB of one row.
+    const int a_oct = lane & 15;
+    const int a_base = (lane >> 4) * kBuf + (((a_oct >> 2) * MB) * 64 + 16 * (a_oct & 3)) * 16;
+    // Rows at or past m are neither loaded nor stored: they only feed MFMA
+    // output columns that are never written back.
+    uint32_t aoff[QB];
+    int ldst[QB];
+    bool alive[QB];
+#pragma unroll
+    for (int u = 0; u < QB; ++u) {
+        const int row = min(wn + NWN * u, kRows - 1);
+        alive[u] = row < M;
+        aoff[u] = (uint32_t)(row * K + 8 * lane) * 2u;
+        ldst[u] = a_base + ((row >> 4) * 64 + ((row & 15) ^ a_oct)) * 16;
+    }
+    uint8_t* const ring = lds_a + wk * 2 * kBlk;
+
+    f32x4 acc[TN][MB];
+#pragma unroll
+    for (int tt = 0; tt < TN; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 wr[4][TN];
+    u32x4 ar[QB];
+    SW sa[TN], sbs[TN];
+    // activations of block sbx into registers
+    auto a_issue = [&](int sbx) {
+        const bool in_k = sbx * kScaleBlockK + 8 * lane < K;  // K tail reads zeros
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+            const uint32_t off = aoff[u] + (uint32_t)sbx * (kScaleBlockK * 2);
+            if (alive[u]) ar[u] = load_a(ra, in_k ? off : kOutOfRange);
+        }
+    };
+    auto a_store = [&](int buf) {
+        uint8_t* dst = ring + buf * kBlk;
+#pragma unroll
+        for (int u = 0; u < QB; ++u)
+            if (alive[u]) *reinterpret_cast<u32x4*>(dst + ldst[u]) = ar[u];
+    };
+    auto w_issue = [&](auto slot_c, int chunk) {
+        constexpr int SL = decltype(slot_c)::value;
+        chunk = min(chunk, cmax);
+#pragma unroll
+        for (int tt = 0; tt < TN; ++tt)
+            wr[SL][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, kLoadStream);
+    };
+    auto lds_barrier = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    // multiply chunk T of the block in LDS buffer buf with code slot T
+    auto compute = [&](auto slot_c, const uint8_t* blk_base, const SW (&sc)[TN]) {
+        constexpr int T = decltype(slot_c)::value;
+        const uint8_t* base = blk_base + T * kBuf;
+        auto step = [&](auto ii) {
+            constexpr int I = decltype(ii)::value;
+            u32x4 a[MB];
+            const int slot = 16 * j + (r ^ (4 * I + j));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                a[mb] = *reinterpret_cast<const u32x4*>(base + ((I * MB + mb) * 64 + slot) * 16);
+#pragma unroll
+            for (int tt = 0; tt < TN; ++tt) {
+                const u32x4 wf = dequant_step<FMT, T, I, ACT>(wr[T][tt], sc[tt]);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = mfma<ACT>(wf, a[mb], acc[tt][mb]);
+            }
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+    };
+    auto pstep = [&](auto slot_c, int base, bool valid, const uint8_t* blk_base, const SW (&cur)[TN]) {
+        constexpr int T = decltype(slot_c)::value;
+        w_issue(std::integral_constant<int, (T + 3) % 4>{}, base + T + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        if (valid) compute(slot_c, blk_base, cur);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // one 512-K block (x = blk, LDS buffer PAR = blk % 2): chunks 4 (sb0 + blk)
+    // .. +3 with scales cur; prefetches the next block's scales into nxt and
+    // its activations into registers, and stores those to the other buffer.
+    auto block = [&](auto par_c, int blk, const SW (&cur)[TN], SW (&nxt)[TN]) {
+        constexpr int PAR = decltype(par_c)::value;
+        const int base = 4 * (sb0 + blk);
+        const bool valid = blk < own;
+        const int nsb = min(sb0 + blk + 1, sbmax);
+        lds_barrier();
+        a_issue(nsb);
+#pragma unroll
+        for (int tt = 0; tt < TN; ++tt) nxt[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
+        const uint8_t* blk_base = ring + PAR * kBlk;
+        pstep(std::integral_constant<int, 0>{}, base, valid, blk_base, cur);
+        pstep(std::integral_constant<int, 1>{}, base, valid, blk_base, cur);
+        pstep(std::integral_constant<int, 2>{}, base, valid, blk_base, cur);
+        pstep(std::integral_constant<int, 3>{}, base, valid, blk_base, cur);
+        a_store(1 - PAR);
+    };
+
+    const int c0 = 4 * sb0;
+    a_issue(min(sb0, sbmax));
+#pragma unroll
+    for (int tt = 0; tt < TN; ++tt) sa[tt] = load_scale_block<FMT>(rs[tt], soff, min(sb0, sbmax));
+    w_issue(std::integral_constant<int, 0>{}, c0);
+    w_issue(std::integral_constant<int, 1>{}, c0 + 1);
+    w_issue(std::integral_constant<int, 2>{}, c0 + 2);
+    a_store(0);
+    int blk = 0;
+    for (; blk + 1 < nblk; blk += 2) {
+        block(std::integral_constant<int, 0>{}, blk, sa, sbs);
+        block(std::integral_constant<int, 1>{}, blk + 1, sbs, sa);
+    }
+    if (blk < nblk) block(std::integral_constant<int, 0>{}, blk, sa, sbs);
+
+    if constexpr (NWK > 1) {
+        __shared__ f32x4 red[(NWK - 1) * NWN * TN * MB * kLanes];
+        if (wk > 0) {
+#pragma unroll
+            for (int tt = 0; tt < TN; ++tt)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    red[((((wk - 1) * NWN + wn) * TN + tt) * MB + mb) * kLanes + lane] = acc[tt][mb];
+        }
+        __syncthreads();
+        if (wk != 0) return;
+        for (int g = 1; g < NWK; ++g)
+#pragma unroll
+            for (int tt = 0; tt < TN; ++tt)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[tt][mb] += red[((((g - 1) * NWN + wn) * TN + tt) * MB + mb) * kLanes + lane];
+    }
+#pragma unroll
+    for (int tt = 0; tt < TN; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
+            if (P == nullptr) {
+                store_frag<ACT>(C, acc[tt][mb], m, n0, M, N);
+            } else if (m < M) {
+                float* dst = P + ((size_t)ks * M + m) * N + n0;
+                if ((N & 3) == 0 && n0 + 3 < N) {
+                    *reinterpret_cast<f32x4*>(dst) = acc[tt][mb];
+                } else {
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + e < N) dst[e] = acc[tt][mb][e];
+                }
+            }
+        }
+}
+
+// Y = sum over s of the S partial products P[s][M][N] (in order s = 0, 1, ...),
+// rounded to BF16.  Four consecutive elements of the flattened [M][N] array
+// per thread.
+template <int ACT>
+__global__ __launch_bounds__(256) void reduce_partials(const float* __restrict__ P, uint16_t* __restrict__ C,
+                                                       int64_t total, int S) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= total) return;
+    if (e + 3 < total) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(P + e);
+        for (int s = 1; s < S; ++s) v += *reinterpret_cast<const f32x4*>(P + (size_t)s * total + e);
+        u32x2 o = {pack_out<ACT>(v.x, v.y), pack_out<ACT>(v.z, v.w)};
+        *reinterpret_cast<u32x2*>(C + e) = o;
+    } else {
+        for (int64_t x = e; x < total; ++x) {
+            float v = P[x];
+            for (int s = 1; s < S; ++s) v += P[(size_t)s * total + x];
+            C[x] = (uint16_t)(pack_out<ACT>(v, 0.f) & 0xFFFF);
+        }
+    }
+}
+
+// ----------------------------------------------------------- prefill GEMM
+// Larger m.  A 256-thread workgroup computes a BM (m) x BN (n) tile with its
+// four waves in a WM x WN grid (a wave owns MBW 16-row m-blocks and TNW
+// n-tiles), over a K range (the whole K, or 1/S of it with FP32 partials).
+// Per 128-K chunk c:
+//   issue the activations of chunk c+2 into register set c % 2 and the code
+//   blocks of chunk c+3 into ring slot (c+3) % 4 (scales one 512-K block
+//   ahead), multiply chunk c from LDS buffer c % 2 and ring slot c % 4, write
+//   the activations of chunk c+1 (issued one step earlier) to LDS buffer
+//   (c+1) % 2, barrier (LDS only).
+// Loads are issued in the order they are waited for, so the wait before each
+// LDS write leaves the younger code prefetches in flight.  The activation
+// tile is XOR-swizzled by row in LDS (conflict-free 16-byte writes and
+// fragment reads; the Petit blog, "Mastering the memory hierarchy").
+template <int FMT, int ACT, int WM, int WN, int MBW, int TNW, bool KTAIL>
+__global__ __launch_bounds__(256) void gemm_prefill(const uint16_t* __restrict__ A, const u32x4* __restrict__ wq,
+                                                   const uint8_t* __restrict__ sq, uint16_t* __restrict__ C,
+                                                   float* __restrict__ P, int M, int N, int K, int KB, int SB, int NT,
+                                                   int S) {
+    static_assert(WM * WN == 4, "four waves");
+    typedef u32x4 SW;
+    constexpr int BM = WM * MBW * 16;  // m rows per workgroup
+    constexpr int BNT = WN * TNW;      // n-tiles per workgroup
+    constexpr int kBuf = BM * 256;     // one LDS activation buffer (BM x 128 K x 2 B)
+    constexpr int kStage = BM / 16;    // 16-byte activation pieces per thread per chunk
+    constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kBuf];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, j = lane >> 4;
+    const int wm = wave % WM, wn = wave / WM;
+
+    // work item: K split ks (innermost), then an XCD-banded (m-tile, n-group) order
+    const int MT = (M + BM - 1) / BM, NG = (NT + BNT - 1) / BNT;
+    const int ks = blockIdx.x % S;
+    const int item = blockIdx.x / S;
+    const int total = MT * NG;
+    int L = item;
+    if (total % kXcdCount == 0 && S == 1)
+        L = (item % kXcdCount) * (total / kXcdCount) + item / kXcdCount;
+    const int mt = L % MT, ng = L / MT;
+    const int m0 = mt * BM;
+    const int tile0 = ng * BNT + wn * TNW;
+    const int sb0 = (ks * SB) / S, sb1 = ((ks + 1) * SB) / S;
+    const int c0 = 4 * sb0, clast = 4 * sb1 - 1;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(M * K * 2));
+    const int soff = scale_lane_offset<FMT>(r, j);
+    __amdgpu_buffer_rsrc_t rw[TNW], rs[TNW];
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt) {
+        const int t = min(tile0 + tt, NT - 1);
+        rw[tt] = make_rsrc(reinterpret_cast<const uint8_t*>(wq) + (size_t)t * KB * 1024, (uint32_t)KB * 1024u);
+        rs[tt] = make_rsrc(sq + (size_t)t * SB * kScaleBlockBytes, (uint32_t)(SB * kScaleBlockBytes));
+    }
+
+    // activation staging: piece q of this thread = (row, 16-byte column)
+    uint32_t aoff[kStage];
+    int lds_off[kStage];
+#pragma unroll
+    for (int q = 0; q < kStage; ++q) {
+        const int idx = tid + 256 * q;
+        const int row = idx >> 4, col = idx & 15;
+        aoff[q] = (uint32_t)((m0 + row) * K + col * 8) * 2u;
+        lds_off[q] = row * 256 + ((col ^ (row & 15)) << 4);
+    }
+    u32x4 st[2][kStage];
+    auto a_issue = [&](auto set_c, int chunk) {
+        constexpr int SET = decltype(set_c)::value;
+        chunk = min(chunk, clast);
+#pragma unroll
+        for (int q = 0; q < kStage; ++q) {
+            const int k = chunk * kChunkK + (((tid + 256 * q) & 15) * 8);
+            const uint32_t off = aoff[q] + (uint32_t)(chunk * kChunkK) * 2u;
+            st[SET][q] = load_a(ra, (!KTAIL || k < K) ? off : kOutOfRange);
+        }
+    };
+    auto a_store = [&](auto set_c) {
+        constexpr int SET = decltype(set_c)::value;
+#pragma unroll
+        for (int q = 0; q < kStage; ++q) *reinterpret_cast<u32x4*>(lds_a + SET * kBuf + lds_off[q]) = st[SET][q];
+    };
+    u32x4 wr[4][TNW];
+    auto w_issue = [&](auto slot_c, int chunk) {
+        constexpr int SL = decltype(slot_c)::value;
+        chunk = min(chunk, clast);
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt)
+            wr[SL][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, kLoadStream);
+    };
+    auto lds_barrier = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    f32x4 acc[TNW][MBW];
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // multiply chunk (position T in its 512-K block) from LDS buffer BUF.
+    // The dequant of tile tt+1 is placed before the products of tile tt and
+    // the scheduler is asked to alternate one matrix instruction with two
+    // vector instructions, so the dequant runs while the matrix core works.
+    auto compute = [&](auto t_c, auto buf_c, const SW (&sc)[TNW]) {
+        constexpr int T = decltype(t_c)::value;
+        constexpr int BUF = decltype(buf_c)::value;
+        const uint8_t* base = lds_a + BUF * kBuf;
+        auto step = [&](auto ii) {
+            constexpr int I = decltype(ii)::value;
+            u32x4 a[MBW];
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb) {
+                const int row = wm * MBW * 16 + mb * 16 + r;
+                const int col = 4 * I + j;
+                a[mb] = *reinterpret_cast<const u32x4*>(base + row * 256 + ((col ^ (row & 15)) << 4));
+            }
+            u32x4 wf[TNW];
+            wf[0] = dequant_step<FMT, T, I, ACT>(wr[T][0], sc[0]);
+#pragma unroll
+            for (int tt = 0; tt < TNW; ++tt) {
+                if (tt + 1 < TNW) wf[tt + 1] = dequant_step<FMT, T, I, ACT>(wr[T][tt + 1], sc[tt + 1]);
+#pragma unroll
+                for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = mfma<ACT>(wf[tt], a[mb], acc[tt][mb]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, MBW, 0);  // fragment reads first
+#pragma unroll
+            for (int q = 0; q < MBW * TNW; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+            }
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+    };
+    // step for chunk c = base + T (T = c % 4; c % 2 == T % 2)
+    auto pstep = [&](auto t_c, int base, const SW (&cur)[TNW]) {
+        constexpr int T = decltype(t_c)::value;
+        a_issue(std::integral_constant<int, T % 2>{}, base + T + 2);
+        w_issue(std::integral_constant<int, (T + 3) % 4>{}, base + T + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t_c, std::integral_constant<int, T % 2>{}, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        a_store(std::integral_constant<int, (T + 1) % 2>{});
+        lds_barrier();
+    };
+    SW sa[TNW], sbs[TNW];
+    auto block = [&](int sbx, const SW (&cur)[TNW], SW (&nxt)[TNW]) {
+        const int base = 4 * sbx;
+        const int nsb = min(sbx + 1, sb1 - 1);
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt) nxt[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
+        pstep(std::integral_constant<int, 0>{}, base, cur);
+        pstep(std::integral_constant<int, 1>{}, base, cur);
+        pstep(std::integral_constant<int, 2>{}, base, cur);
+        pstep(std::integral_constant<int, 3>{}, base, cur);
+    };
+
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt) sa[tt] = load_scale_block<FMT>(rs[tt], soff, sb0);
+    a_issue(std::integral_constant<int, 0>{}, c0);
+    w_issue(std::integral_constant<int, 0>{}, c0);
+    w_issue(std::integral_constant<int, 1>{}, c0 + 1);
+    w_issue(std::integral_constant<int, 2>{}, c0 + 2);
+    a_issue(std::integral_constant<int, 1>{}, c0 + 1);
+    a_store(std::integral_constant<int, 0>{});
+    lds_barrier();
+    int sb = sb0;
+    for (; sb + 1 < sb1; sb += 2) {
+        block(sb, sa, sbs);
+        block(sb + 1, sbs, sa);
+    }
+    if (sb < sb1) block(sb, sa, sbs);
+
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+            const int m = m0 + wm * MBW * 16 + mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
+            if (P == nullptr) {
+                store_frag<ACT>(C, acc[tt][mb], m, n0, M, N);
+            } else if (m < M) {
+                float* dst = P + ((size_t)ks * M + m) * N + n0;
+                if ((N & 3) == 0 && n0 + 3 < N) {
+                    *reinterpret_cast<f32x4*>(dst) = acc[tt][mb];
+                } else {
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + e < N) dst[e] = acc[tt][mb][e];
+                }
+            }
+        }
+}
+
+// ------------------------------------------------------------ debug dequant
+// One wave per (n-tile, 128-K chunk): writes the BF16 weights it would feed to
+// the matrix core, using the GEMM's own dequant functions.
+template <int FMT, int ACT>
+__global__ __launch_bounds__(64) void dequant_kernel(const u32x4* __restrict__ wq, const uint8_t* __restrict__ sq,
+                                                     uint16_t* __restrict__ W, int N, int K, int KB, int SB) {
+    typedef u32x4 SW;
+    const int t = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x, r = lane & 15, j = lane >> 4;
+    const int n = t * kTileN + r;
+    const u32x4 w = wq[((size_t)t * KB + b) * kLanes + lane];
+    const SW s = *reinterpret_cast<const u32x4*>(sq + ((size_t)t * SB + b / 4) * scale_block_bytes<FMT>() +
+                                                 scale_lane_offset<FMT>(r, j));
+    u32x4 o[4];
+    switch (b & 3) {
+        case 0: o[0] = dequant_step<FMT, 0, 0, ACT>(w, s); o[1] = dequant_step<FMT, 0, 1, ACT>(w, s);
+                o[2] = dequant_step<FMT, 0, 2, ACT>(w, s); o[3] = dequant_step<FMT, 0, 3, ACT>(w, s); break;
+        case 1: o[0] = dequant_step<FMT, 1, 0, ACT>(w, s); o[1] = dequant_step<FMT, 1, 1, ACT>(w, s);
+                o[2] = dequant_step<FMT, 1, 2, ACT>(w, s); o[3] = dequant_step<FMT, 1, 3, ACT>(w, s); break;
+        case 2: o[0] = dequant_step<FMT, 2, 0, ACT>(w, s); o[1] = dequant_step<FMT, 2, 1, ACT>(w, s);
+                o[2] = dequant_step<FMT, 2, 2, ACT>(w, s); o[3] = dequant_step<FMT, 2, 3, ACT>(w, s); break;
+        default: o[0] = dequant_step<FMT, 3, 0, ACT>(w, s); o[1] = dequant_step<FMT, 3, 1, ACT>(w, s);
+                 o[2] = dequant_step<FMT, 3, 2, ACT>(w, s); o[3] = dequant_step<FMT, 3, 3, ACT>(w, s); break;
+    }
+    if (n >= N) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = b * kChunkK + 32 * i + 8 * j;
+        if (k < K) *reinterpret_cast<u32x4*>(W + (size_t)n * K + k) = o[i];
+    }
+}
+
+}  // namespace fp4

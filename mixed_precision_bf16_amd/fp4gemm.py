@@ -33,7 +33,10 @@ _SIGNATURES = {
     "fp4_gemm_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.POINTER(_c_sz)]),
     "fp4_gemm": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_vp, _c_sz,
                                 _c_vp]),
+    "fp4_gemm_f16": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_vp,
+                                    _c_sz, _c_vp]),
     "fp4_dequant": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
+    "fp4_dequant_f16": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
 }
 
 STATUS = {0: "FP4_OK", 1: "FP4_ERR_NULL", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_FORMAT", 4: "FP4_ERR_VALUE",
@@ -145,11 +148,12 @@ def new_workspace(m: int, N: int, K: int, fmt: int, device="cuda"):
 
 
 def gemm(A, wq, sq, N: int, K: int, fmt: int, out=None, workspace=None, stream=None):
-    """Y = A . dequant(W)^T.  A: bf16 CUDA [m][K]; wq, sq: uint8 CUDA (packed).
-    Returns (or fills) a bf16 CUDA tensor [m][N]."""
+    """Y = A . dequant(W)^T.  A: bfloat16 (fp4_gemm) or float16 (fp4_gemm_f16)
+    CUDA [m][K]; wq, sq: uint8 CUDA (packed).  Returns (or fills) a tensor
+    [m][N] of A's dtype."""
     import torch
-    if A.dtype != torch.bfloat16 or A.dim() != 2 or not A.is_cuda or not A.is_contiguous():
-        raise ValueError("A must be a contiguous 2-D bfloat16 CUDA tensor")
+    if A.dtype not in (torch.bfloat16, torch.float16) or A.dim() != 2 or not A.is_cuda or not A.is_contiguous():
+        raise ValueError("A must be a contiguous 2-D bfloat16 or float16 CUDA tensor")
     if A.shape[1] != K:
         raise ValueError("A must have K columns")
     for t in (wq, sq):
@@ -160,28 +164,35 @@ def gemm(A, wq, sq, N: int, K: int, fmt: int, out=None, workspace=None, stream=N
         raise ValueError("packed weight tensors have the wrong size")
     m = A.shape[0]
     if out is None:
-        out = torch.empty((m, N), dtype=torch.bfloat16, device=A.device)
-    elif out.shape != (m, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor [m][N]")
+        out = torch.empty((m, N), dtype=A.dtype, device=A.device)
+    elif out.shape != (m, N) or out.dtype != A.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor [m][N] of A's dtype")
     wsb = workspace_size(m, N, K, fmt)
     if wsb and workspace is None:
         workspace = torch.zeros(wsb, dtype=torch.uint8, device=A.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().fp4_gemm(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), m, N, K, fmt,
-                          _dev_ptr(workspace), ws_bytes, _stream_handle(stream)), "fp4_gemm")
+    fn = lib().fp4_gemm if A.dtype == torch.bfloat16 else lib().fp4_gemm_f16
+    _check(fn(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), m, N, K, fmt, _dev_ptr(workspace), ws_bytes,
+              _stream_handle(stream)), "fp4_gemm")
     return out
 
 
-def dequant(wq, sq, N: int, K: int, fmt: int, out=None, stream=None):
-    """BF16 weights [N][K] exactly as the GEMM feeds them to the matrix core."""
+def dequant(wq, sq, N: int, K: int, fmt: int, out=None, stream=None, dtype=None):
+    """Weights [N][K] exactly as the GEMM feeds them to the matrix core:
+    bfloat16 (default) or float16 (dtype=torch.float16)."""
     import torch
+    dtype = torch.bfloat16 if dtype is None else dtype
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("dtype must be torch.bfloat16 or torch.float16")
     nw, ns = repack_size(N, K, fmt)
     if wq.numel() != nw or sq.numel() != ns or not wq.is_cuda or not sq.is_cuda:
         raise ValueError("packed weight tensors have the wrong size or device")
     if out is None:
-        out = torch.empty((N, K), dtype=torch.bfloat16, device=wq.device)
-    _check(lib().fp4_dequant(_dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), N, K, fmt, _stream_handle(stream)),
-           "fp4_dequant")
+        out = torch.empty((N, K), dtype=dtype, device=wq.device)
+    elif out.shape != (N, K) or out.dtype != dtype or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous CUDA tensor [N][K] of the requested dtype")
+    fn = lib().fp4_dequant if dtype == torch.bfloat16 else lib().fp4_dequant_f16
+    _check(fn(_dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), N, K, fmt, _stream_handle(stream)), "fp4_dequant")
     return out
 
 

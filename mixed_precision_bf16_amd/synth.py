@@ -14,7 +14,8 @@ stand in for them:
   petit-kernel page, "Known limitations": inputs carry no negative zeros);
 * NVFP4 scales: E4M3 rounding (round to nearest even) of 2^u, u ~ U(-4, 2);
 * MXFP4 scales: E8M0 byte 127 + e, e uniform over the integers -6..2;
-* A: float32 N(0, 1) rounded to BF16 (nearest even).
+* A: float32 N(0, 1) rounded to BF16 (nearest even), or to FP16 for the
+  FP16-activation variant (``act="f16"``; same float32 draws).
 
 The edge sweep adds 1 % outliers ~ N(0, sd 10) to A, forces row 0's first 16
 codes to cover every code except negative zero (including +-6 and 0) and forces
@@ -46,7 +47,7 @@ LLAMA3_70B_LAYERS = (
 
 @dataclass
 class Problem:
-    """One GEMM instance: A [m][K] BF16 bits, codes [N][K/2], scales [N][K/G]."""
+    """One GEMM instance: A [m][K] BF16 (or FP16) bits, codes [N][K/2], scales [N][K/G]."""
     name: str
     m: int
     N: int
@@ -56,6 +57,7 @@ class Problem:
     codes: np.ndarray
     scales: np.ndarray
     seed: int
+    act: str = "bf16"
 
     @property
     def group(self) -> int:
@@ -105,6 +107,19 @@ def _bf16_bits_of(values_f32: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def _f16_bits_of(values_f32: np.ndarray) -> np.ndarray:
+    """Round float32 values to FP16 with the library cast (nearest even)."""
+    return np.ascontiguousarray(values_f32, dtype=np.float32).astype(np.float16).view(np.uint16).copy()
+
+
+def _act_bits_of(values_f32: np.ndarray, act: str) -> np.ndarray:
+    if act == "bf16":
+        return _bf16_bits_of(values_f32)
+    if act == "f16":
+        return _f16_bits_of(values_f32)
+    raise ValueError(f"unknown activation type {act}")
+
+
 def _draw_scales(rng, N, K, fmt):
     G = GROUP[fmt]
     if fmt == FMT_NVFP4:
@@ -114,11 +129,11 @@ def _draw_scales(rng, N, K, fmt):
     return (127 + e).astype(np.uint8)
 
 
-def _draw_a(rng, m, K):
-    return _bf16_bits_of(rng.standard_normal(size=(m, K), dtype=np.float32))
+def _draw_a(rng, m, K, act="bf16"):
+    return _act_bits_of(rng.standard_normal(size=(m, K), dtype=np.float32), act)
 
 
-def make_problem(config: int, shape_idx: int, m_idx: int) -> Problem:
+def make_problem(config: int, shape_idx: int, m_idx: int, act: str = "bf16") -> Problem:
     """Build the seeded inputs of one case of one workload config."""
     for (name, si, mi, m, N, K, fmt) in config_cases(config):
         if si == shape_idx and mi == m_idx:
@@ -129,17 +144,17 @@ def make_problem(config: int, shape_idx: int, m_idx: int) -> Problem:
     rng = np.random.Generator(np.random.PCG64(seed))
     codes = _draw_codes(rng, N, K)
     scales = _draw_scales(rng, N, K, fmt)
-    a_bits = _draw_a(rng, m, K)
+    a_bits = _draw_a(rng, m, K, act)
     if config == 4:
-        _edge_overrides(rng, a_bits, codes, m, N, K)
-    return Problem(name, m, N, K, fmt, a_bits, codes, scales, seed)
+        _edge_overrides(rng, a_bits, codes, m, N, K, act)
+    return Problem(name, m, N, K, fmt, a_bits, codes, scales, seed, act)
 
 
-def _edge_overrides(rng, a_bits, codes, m, N, K):
+def _edge_overrides(rng, a_bits, codes, m, N, K, act="bf16"):
     # 1 % of A replaced by N(0, sd 10) outliers.
     mask = rng.random(size=(m, K)) < 0.01
     out = rng.standard_normal(size=(m, K), dtype=np.float32) * np.float32(10.0)
-    a_bits[mask] = _bf16_bits_of(out)[mask]
+    a_bits[mask] = _act_bits_of(out, act)[mask]
     # Row 0, k = 0..15: every code except negative zero, then code 7 (+6).
     seq = np.array([0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15, 7], dtype=np.uint8)
     codes[0, 0:8] = seq[0::2] | (seq[1::2] << 4)
@@ -149,7 +164,7 @@ def _edge_overrides(rng, a_bits, codes, m, N, K):
 
 def make_random(m: int, N: int, K: int, fmt: int, seed: int, *,
                 scale_lo: float = -4.0, scale_hi: float = 2.0,
-                allow_neg_zero: bool = False, a_scale: float = 1.0) -> Problem:
+                allow_neg_zero: bool = False, a_scale: float = 1.0, act: str = "bf16") -> Problem:
     """Free-shape case with the same distributions (for ragged/edge tests)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     G = GROUP[fmt]
@@ -165,5 +180,5 @@ def make_random(m: int, N: int, K: int, fmt: int, seed: int, *,
         e = rng.integers(int(scale_lo), int(scale_hi) + 1, size=(N, K // G))
         scales = (127 + e).astype(np.uint8)
     a = rng.standard_normal(size=(m, K), dtype=np.float32) * np.float32(a_scale)
-    a_bits = _bf16_bits_of(a)
-    return Problem(f"rand_m{m}_N{N}_K{K}_f{fmt}", m, N, K, fmt, a_bits, codes, scales, seed)
+    a_bits = _act_bits_of(a, act)
+    return Problem(f"rand_m{m}_N{N}_K{K}_f{fmt}_{act}", m, N, K, fmt, a_bits, codes, scales, seed, act)

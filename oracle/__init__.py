@@ -21,6 +21,9 @@ from .fp4_oracle import (  # noqa: F401
     e2m1_value,
     e4m3_value,
     e8m0_value,
+    fp16_bits_of_exact,
+    fp16_bits_to_f64,
+    act_bits_to_f64,
     gemm_reference,
     group_size,
     scale_value,

@@ -30,7 +30,9 @@ What is computed, and where the pages say so
 
 Storage conventions (read where the pages are silent)
 -----------------------------------------------------
-* A: uint16 array [m][K] of BF16 bit patterns, row-major.
+* A: uint16 array [m][K] of BF16 bit patterns, row-major (or FP16 bit
+  patterns for the FP16-activation variant of the same kernels, which the
+  Petit blog's introduction names alongside BF16).
 * codes: uint8 array [N][K/2]; byte j of row n holds element k = 2j in bits
   3..0 and k = 2j + 1 in bits 7..4 (two FP4 values per byte, mhpq.cn article
   section 3.3; which nibble comes first is not stated).
@@ -167,15 +169,52 @@ def bf16_bits_of_exact(values: np.ndarray) -> np.ndarray:
     return (bits >> 16).astype(np.uint16)
 
 
+def fp16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns -> float64, decoded from the fields:
+    sign = bit 15, exponent = bits 14..10 (bias 15), mantissa = bits 9..0;
+    exponent 0 is subnormal (f/1024 x 2^-14), exponent 31 is Inf (f = 0) or
+    NaN."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = (b >> 15) & 1
+    exp = (b >> 10) & 31
+    man = b & 1023
+    subnormal = (man / 1024.0) * 2.0 ** -14
+    normal = (1.0 + man / 1024.0) * np.exp2(exp.astype(np.float64) - 15.0)
+    mag = np.where(exp == 0, subnormal, normal)
+    mag = np.where(exp == 31, np.where(man == 0, np.inf, np.nan), mag)
+    return np.where(sign == 1, -mag, mag).astype(np.float64)
+
+
+def fp16_bits_of_exact(values: np.ndarray) -> np.ndarray:
+    """FP16 bit patterns of float64 values that are exactly representable in
+    FP16; raises if any value is not."""
+    v = np.asarray(values, dtype=np.float64)
+    h = v.astype(np.float16)
+    finite = np.isfinite(v)
+    if np.any(finite & (h.astype(np.float64) != v)):
+        raise ValueError("value not exactly representable in FP16")
+    return h.view(np.uint16)
+
+
+def act_bits_to_f64(bits: np.ndarray, act: str = "bf16") -> np.ndarray:
+    """Activation / output bit patterns (BF16 or FP16) -> float64."""
+    if act == "bf16":
+        return bf16_bits_to_f64(bits)
+    if act == "f16":
+        return fp16_bits_to_f64(bits)
+    raise ValueError(f"unknown activation type {act}")
+
+
 def gemm_reference(a_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray,
-                   K: int, fmt: int):
+                   K: int, fmt: int, act: str = "bf16"):
     """Y_ref[i][n] = sum_k a[i][k] w[n][k] and B[i][n] = sum_k |a[i][k] w[n][k]|.
 
     Both in float64 with a library matrix product (the error of the float64 sum
-    is below K * 2^-53 * B, negligible against the tolerance).  Returns
-    (y_ref, bound), each [m][N].
+    is below K * 2^-53 * B, negligible against the tolerance).  `act` names
+    the type of the activation bits (BF16 or FP16).  Returns (y_ref, bound),
+    each [m][N].
     """
-    a = bf16_bits_to_f64(a_bits)
+    a = act_bits_to_f64(a_bits, act)
     if a.ndim != 2 or a.shape[1] != K:
         raise ValueError("A must be [m][K]")
     w = dequant_weights(codes, scales, K, fmt)
@@ -185,12 +224,13 @@ def gemm_reference(a_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray,
 
 
 def check_tolerance(y_bits: np.ndarray, y_ref: np.ndarray, bound: np.ndarray,
-                    rel: float = 8e-3, abs_of_bound: float = 2e-3) -> np.ndarray:
+                    rel: float = 8e-3, abs_of_bound: float = 2e-3, act: str = "bf16") -> np.ndarray:
     """Element-wise pass mask: y finite and |y - y_ref| <= rel*|y_ref| + abs_of_bound*B.
 
-    The bound covers BF16 round-to-nearest of the output (<= 2^-9 relative)
-    plus any FP32 summation order over K <= 33554 terms (<= K 2^-24 B).
+    The bound covers BF16 round-to-nearest of the output (<= 2^-9 relative;
+    FP16: 2^-11) plus any FP32 summation order over K <= 33554 terms
+    (<= K 2^-24 B).
     """
-    y = bf16_bits_to_f64(y_bits)
+    y = act_bits_to_f64(y_bits, act)
     err = np.abs(y - y_ref)
     return np.isfinite(y) & (err <= rel * np.abs(y_ref) + abs_of_bound * bound)

@@ -145,8 +145,10 @@ def test_shape_and_format_errors(N, K, fmt, status):
     assert F.lib().fp4_repack_size(N, K, fmt, ctypes.byref(sz), ctypes.byref(sz)) == status
     assert F.lib().fp4_gemm_workspace_size(16, N, K, fmt, ctypes.byref(sz)) == status
     dummy = ctypes.c_void_p(1)
-    assert F.lib().fp4_gemm(dummy, dummy, dummy, dummy, 16, N, K, fmt, None, 0, None) == status
-    assert F.lib().fp4_dequant(dummy, dummy, dummy, N, K, fmt, None) == status
+    for gemm in (F.lib().fp4_gemm, F.lib().fp4_gemm_f16):
+        assert gemm(dummy, dummy, dummy, dummy, 16, N, K, fmt, None, 0, None) == status
+    for deq in (F.lib().fp4_dequant, F.lib().fp4_dequant_f16):
+        assert deq(dummy, dummy, dummy, N, K, fmt, None) == status
 
 
 def test_gemm_argument_errors_before_any_hip_call():
@@ -161,6 +163,10 @@ def test_gemm_argument_errors_before_any_hip_call():
     assert lib.fp4_gemm(d, d, d, d, (1 << 20) + 1, 64, 64, 0, None, 0, None) == 2
     # m = 0 is a no-op, even with null pointers
     assert lib.fp4_gemm(z, z, z, z, 0, 64, 64, 0, None, 0, None) == 0
+    assert lib.fp4_gemm_f16(z, z, z, z, 0, 64, 64, 0, None, 0, None) == 0
+    for args in ((z, d, d, d), (d, d, d, z)):
+        assert lib.fp4_gemm_f16(*args, 16, 64, 64, 0, None, 0, None) == 1
+    assert lib.fp4_dequant_f16(d, z, d, 4, 32, 0, None) == 1
     # A bytes beyond the 32-bit buffer range
     assert lib.fp4_gemm(d, d, d, d, 1 << 20, 64, 1024, 0, None, 0, None) == 2
     # repack / unpack / dequant null pointers

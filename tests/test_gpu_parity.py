@@ -1,8 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
+Both activation types are covered: BF16 (``fp4_gemm``, ``fp4_dequant``) and
+FP16 (``fp4_gemm_f16``, ``fp4_dequant_f16``).
+
 Bars:
-* dequantized weights (``fp4_dequant`` and a one-hot activation probe through
-  ``fp4_gemm`` itself) are bit-exact against the oracle's BF16 weights;
+* dequantized weights (``fp4_dequant[_f16]`` and a one-hot activation probe
+  through the GEMM itself) are bit-exact against the oracle's weights;
 * GEMM outputs satisfy |y - y_ref| <= 8e-3 |y_ref| + 2e-3 sum_k |a_k w_k|
   element by element (oracle.check_tolerance), with every output finite.
 Full-size workloads are compared on sampled output columns (rows of W) that
@@ -37,8 +40,16 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def _to_dev_a(a_bits):
-    return torch.from_numpy(np.ascontiguousarray(a_bits).view(np.int16)).cuda().view(torch.bfloat16)
+def _tdt(act):
+    return torch.bfloat16 if act == "bf16" else torch.float16
+
+
+def _to_dev_a(a_bits, act="bf16"):
+    return torch.from_numpy(np.ascontiguousarray(a_bits).view(np.int16)).cuda().view(_tdt(act))
+
+
+def _exact_bits(w, act):
+    return oracle.bf16_bits_of_exact(w) if act == "bf16" else oracle.fp16_bits_of_exact(w)
 
 
 def _bits(t):
@@ -48,7 +59,7 @@ def _bits(t):
 def run_gemm(p, reps=1):
     wq, sq = F.repack(p.codes, p.scales, p.N, p.K, p.fmt)
     wq_d, sq_d = F.upload(wq, sq)
-    A = _to_dev_a(p.a_bits)
+    A = _to_dev_a(p.a_bits, p.act)
     outs = []
     for _ in range(reps):
         C = F.gemm(A, wq_d, sq_d, p.N, p.K, p.fmt)
@@ -60,15 +71,15 @@ def run_gemm(p, reps=1):
 def _report(p, ok, y_bits, y_ref, bound, cols=None):
     bad = np.argwhere(~ok)
     i, n = bad[0]
-    y = oracle.bf16_bits_to_f64(y_bits)
+    y = oracle.act_bits_to_f64(y_bits, p.act)
     col = n if cols is None else cols[n]
     return (f"{p.name}: {len(bad)} of {ok.size} outputs out of tolerance; first at m={i}, n={col}: "
             f"gpu={y[i, n]!r} ref={y_ref[i, n]!r} bound={bound[i, n]!r}")
 
 
 def check_full(p, y_bits):
-    y_ref, bound = oracle.gemm_reference(p.a_bits, p.codes, p.scales, p.K, p.fmt)
-    ok = oracle.check_tolerance(y_bits, y_ref, bound)
+    y_ref, bound = oracle.gemm_reference(p.a_bits, p.codes, p.scales, p.K, p.fmt, p.act)
+    ok = oracle.check_tolerance(y_bits, y_ref, bound, act=p.act)
     assert ok.all(), _report(p, ok, y_bits, y_ref, bound)
 
 
@@ -79,22 +90,27 @@ def sample_rows(N, seed, k=192):
 
 
 def check_sampled(p, y_bits):
-    assert np.isfinite(oracle.bf16_bits_to_f64(y_bits)).all(), f"{p.name}: non-finite outputs"
+    assert np.isfinite(oracle.act_bits_to_f64(y_bits, p.act)).all(), f"{p.name}: non-finite outputs"
     rows = sample_rows(p.N, p.seed)
-    y_ref, bound = oracle.gemm_reference(p.a_bits, p.codes[rows], p.scales[rows], p.K, p.fmt)
-    ok = oracle.check_tolerance(y_bits[:, rows], y_ref, bound)
+    y_ref, bound = oracle.gemm_reference(p.a_bits, p.codes[rows], p.scales[rows], p.K, p.fmt, p.act)
+    ok = oracle.check_tolerance(y_bits[:, rows], y_ref, bound, act=p.act)
     assert ok.all(), _report(p, ok, y_bits[:, rows], y_ref, bound, cols=rows)
 
 
 # --------------------------------------------------------- dequant, bit-exact
-def _sweep_problem(fmt, with_neg_zero=False):
+def _sweep_problem(fmt, with_neg_zero=False, act="bf16"):
     """Every code (k = 0..15, then again 16..31) against a sweep of scales, one
     scale per row: all 127 non-negative finite E4M3 bytes, or E8M0 exponents
-    -125..125."""
+    -125..125 (FP16: -23..13, the range where every product is exact)."""
     seq = [0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15, 8 if with_neg_zero else 7]
     row = seq + seq[::-1]
     packed = np.array([row[2 * i] | (row[2 * i + 1] << 4) for i in range(16)], np.uint8)
-    scale_bytes = np.arange(0, 0x7F, dtype=np.uint8) if fmt == 0 else np.arange(2, 253, dtype=np.uint8)
+    if fmt == 0:
+        scale_bytes = np.arange(0, 0x7F, dtype=np.uint8)
+    elif act == "bf16":
+        scale_bytes = np.arange(2, 253, dtype=np.uint8)
+    else:
+        scale_bytes = np.arange(104, 141, dtype=np.uint8)
     N, K = len(scale_bytes), 32
     codes = np.tile(packed, (N, 1))
     G = 16 if fmt == 0 else 32
@@ -102,74 +118,79 @@ def _sweep_problem(fmt, with_neg_zero=False):
     return N, K, codes, scales
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("neg_zero", [False, True])
-def test_dequant_bit_exact_scale_sweep(fmt, neg_zero):
-    N, K, codes, scales = _sweep_problem(fmt, neg_zero)
-    _say("dequant sweep", fmt, neg_zero, N, K)
-    want = oracle.bf16_bits_of_exact(oracle.dequant_weights(codes, scales, K, fmt))
+def test_dequant_bit_exact_scale_sweep(fmt, neg_zero, act):
+    N, K, codes, scales = _sweep_problem(fmt, neg_zero, act)
+    _say("dequant sweep", fmt, neg_zero, act, N, K)
+    want = _exact_bits(oracle.dequant_weights(codes, scales, K, fmt), act)
     wq, sq = F.repack(codes, scales, N, K, fmt)
     wq_d, sq_d = F.upload(wq, sq)
-    got = _bits(F.dequant(wq_d, sq_d, N, K, fmt))
+    got = _bits(F.dequant(wq_d, sq_d, N, K, fmt, dtype=_tdt(act)))
     torch.cuda.synchronize()
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
 @pytest.mark.parametrize("fmt,N,K,seed", [(0, 1000, 8192, 1), (1, 130, 2080, 2), (0, 17, 528, 3), (1, 8, 96, 4)])
-def test_dequant_bit_exact_random(fmt, N, K, seed):
-    p = synth.make_random(1, N, K, fmt, seed, scale_lo=-9 if fmt == 0 else -20, scale_hi=8 if fmt == 0 else 20,
+def test_dequant_bit_exact_random(fmt, N, K, seed, act):
+    hi = 20 if act == "bf16" else 13
+    p = synth.make_random(1, N, K, fmt, seed, scale_lo=-9 if fmt == 0 else -20, scale_hi=8 if fmt == 0 else hi,
                           allow_neg_zero=True)
-    _say("dequant random", fmt, N, K)
-    want = oracle.bf16_bits_of_exact(oracle.dequant_weights(p.codes, p.scales, K, fmt))
+    _say("dequant random", fmt, N, K, act)
+    want = _exact_bits(oracle.dequant_weights(p.codes, p.scales, K, fmt), act)
     wq, sq = F.repack(p.codes, p.scales, N, K, fmt)
     wq_d, sq_d = F.upload(wq, sq)
-    got = _bits(F.dequant(wq_d, sq_d, N, K, fmt))
+    got = _bits(F.dequant(wq_d, sq_d, N, K, fmt, dtype=_tdt(act)))
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("m", [16, 32, 128])
-def test_one_hot_probe_through_gemm_is_bit_exact(fmt, m):
+def test_one_hot_probe_through_gemm_is_bit_exact(fmt, m, act):
     """A = unit rows: y[i][n] = w[n][i] exactly (one exact product per output),
     so the GEMM's own dequant path is checked bit for bit.  m selects the
     kernel variant (16: one 16-row block, 32: two, 128: the tiled kernel)."""
-    N, K, codes, scales = _sweep_problem(fmt, with_neg_zero=False)
-    _say("one-hot", fmt, m)
+    N, K, codes, scales = _sweep_problem(fmt, with_neg_zero=False, act=act)
+    _say("one-hot", fmt, m, act)
     w = oracle.dequant_weights(codes, scales, K, fmt)
-    want = oracle.bf16_bits_of_exact(w)                     # [N][K]
+    want = _exact_bits(w, act)                              # [N][K]
     wq, sq = F.upload(*F.repack(codes, scales, N, K, fmt))
     for k0 in range(0, K, m):
         rows = min(m, K - k0)
         a = np.zeros((m, K), np.float32)
         for i in range(rows):
             a[i, k0 + i] = 1.0
-        A = torch.from_numpy(a).to(torch.bfloat16).cuda()
+        A = torch.from_numpy(a).to(_tdt(act)).cuda()
         y = _bits(F.gemm(A, wq, sq, N, K, fmt))
         part = want[:, k0:k0 + rows].T
         nz = w[:, k0:k0 + rows].T != 0
         # bit-exact wherever w != 0; a zero weight may come out as +0 or -0
         assert np.array_equal(y[:rows][nz], part[nz])
-        assert not np.any(oracle.bf16_bits_to_f64(y[:rows])[~nz])
-        assert not np.any(oracle.bf16_bits_to_f64(y[rows:])), "zero rows of A give zero"
+        assert not np.any(oracle.act_bits_to_f64(y[:rows], act)[~nz])
+        assert not np.any(oracle.act_bits_to_f64(y[rows:], act)), "zero rows of A give zero"
 
 
 # ------------------------------------------------------------ GEMM parity
-def _worked(name):
+def _worked(name, act="bf16"):
     import json
     import os
     ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))[name]
-    a_bits = torch.tensor(ex["A"], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    a_bits = torch.tensor(ex["A"], dtype=torch.float32).to(_tdt(act)).view(torch.int16).numpy().view(np.uint16)
     return synth.Problem(name, ex["m"], ex["N"], ex["K"], ex["fmt"], a_bits,
-                         np.array(ex["packed_bytes"], np.uint8), np.array(ex["scale_bytes"], np.uint8), 0)
+                         np.array(ex["packed_bytes"], np.uint8), np.array(ex["scale_bytes"], np.uint8), 0, act)
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
 @pytest.mark.parametrize("name", ["nvfp4_2x16", "mxfp4_1x32"])
-def test_worked_examples(name):
-    p = _worked(name)
-    _say("worked example", name)
+def test_worked_examples(name, act):
+    p = _worked(name, act)
+    _say("worked example", name, act)
     y = run_gemm(p)
     want = {"nvfp4_2x16": [[54.0, 2.8125], [0.0, 24.375]], "mxfp4_1x32": [[19.0]]}[name]
-    assert oracle.bf16_bits_to_f64(y).tolist() == want     # exact in BF16
+    assert oracle.act_bits_to_f64(y, act).tolist() == want     # exact in BF16 and FP16
     check_full(p, y)
 
 
@@ -182,6 +203,17 @@ RAGGED = [(1, 16, 16, 0), (5, 40, 48, 0), (16, 100, 512, 0), (17, 130, 544, 1), 
 def test_gemm_ragged_shapes_full_oracle(m, N, K, fmt):
     p = synth.make_random(m, N, K, fmt, seed=m * 7919 + N * 31 + K + fmt)
     _say("ragged", m, N, K, fmt)
+    check_full(p, run_gemm(p))
+
+
+RAGGED_F16 = [(1, 16, 16, 0), (5, 40, 64, 1), (17, 130, 544, 0), (33, 64, 1056, 1), (100, 1000, 1024, 0),
+              (129, 260, 2080, 1), (256, 512, 1024, 0), (300, 96, 640, 1), (7, 8200, 512, 0)]
+
+
+@pytest.mark.parametrize("m,N,K,fmt", RAGGED_F16)
+def test_gemm_f16_ragged_shapes_full_oracle(m, N, K, fmt):
+    p = synth.make_random(m, N, K, fmt, seed=m * 7919 + N * 31 + K + fmt + 5, act="f16")
+    _say("ragged f16", m, N, K, fmt)
     check_full(p, run_gemm(p))
 
 
@@ -220,12 +252,50 @@ def test_config3_mxfp4_sampled(case):
     check_sampled(p, run_gemm(p))
 
 
+@pytest.mark.parametrize("config", [1, 2])
+@pytest.mark.parametrize("case", [0, 2, 3], ids=["qkv", "gate_up", "down"])
+def test_f16_llama_shapes_sampled(config, case):
+    """The decode (m = 16) and prefill (m = 256) Llama 3 70B shapes with FP16
+    activations (same seeded draws, rounded to FP16)."""
+    p = synth.make_problem(config, case, 0, act="f16")
+    _say("f16 config", config, p.name)
+    check_sampled(p, run_gemm(p))
+
+
+@pytest.mark.parametrize("case", [1, 3, 6, 9], ids=lambda i: synth.config_cases(4)[i][0])
+def test_f16_edge_full_oracle(case):
+    c = synth.config_cases(4)[case]
+    p = synth.make_problem(4, c[1], c[2], act="f16")
+    _say("f16 config4", c[0])
+    check_full(p, run_gemm(p))
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
 @pytest.mark.parametrize("m", [16, 256])
-def test_repeat_runs_bit_identical(m):
-    p = synth.make_random(m, 8192, 8192, 0, seed=99)
-    _say("determinism", m)
+def test_repeat_runs_bit_identical(m, act):
+    p = synth.make_random(m, 8192, 8192, 0, seed=99, act=act)
+    _say("determinism", m, act)
     a, b, c = run_gemm(p, reps=3)
     assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_one_workspace_reused_across_shapes_and_calls():
+    # split-K partial sums live in the workspace: stale contents from a call of
+    # another shape must not leak into the next result
+    shapes = [(16, 10240, 8192, 0), (1, 1000, 8192, 0), (16, 8192, 28672, 1), (7, 8200, 8192, 0),
+              (256, 520, 2048, 0)]
+    need = max(F.workspace_size(m, N, K, f) for m, N, K, f in shapes)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for m, N, K, fmt in shapes:
+            _say("workspace reuse", rep, m, N, K, fmt)
+            p = synth.make_random(m, N, K, fmt, seed=31 * m + N + K + fmt)
+            wq, sq = F.repack(p.codes, p.scales, p.N, p.K, p.fmt)
+            wq_d, sq_d = F.upload(wq, sq)
+            C = F.gemm(_to_dev_a(p.a_bits), wq_d, sq_d, p.N, p.K, p.fmt, workspace=ws)
+            torch.cuda.synchronize()
+            check_sampled(p, _bits(C))
 
 
 def test_gemm_writes_into_given_output_on_given_stream():

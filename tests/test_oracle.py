@@ -228,9 +228,82 @@ def pin_tolerance(o):
     assert o.check_tolerance(nan, y_ref, bound).tolist() == [[False, False, True, True]]
 
 
+def pin_fp16_decode_library(o):
+    """Every FP16 bit pattern decodes as the library's IEEE binary16 type."""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = b.view(np.float16).astype(np.float64)
+    got = o.fp16_bits_to_f64(b)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+    assert np.array_equal(o.fp16_bits_of_exact(ref[ok]), b[ok])
+    with pytest.raises(ValueError):
+        o.fp16_bits_of_exact(np.array([1.0 + 2.0 ** -11]))
+
+
+def _all_products(o, fmt, scale_bytes):
+    codes = np.array([[c | (c << 4) for c in range(16)]], dtype=np.uint8)   # 32 elements
+    G = 16 if fmt == 0 else 32
+    c = np.repeat(codes, len(scale_bytes), axis=0)
+    s = np.repeat(np.array(scale_bytes, dtype=np.uint8)[:, None], 32 // G, axis=1)
+    return o.dequant_weights(c, s, 32, fmt)
+
+
+def pin_products_exact_in_fp16(o):
+    """Closed form for the FP16 variant: code x scale has <= 6 significant
+    bits (FP16 keeps 11).  NVFP4: |product| lies in [2^-10, 2688] for every
+    finite positive E4M3 scale, inside FP16's normal range, so every product
+    is exact.  MXFP4: a nonzero product is 2^e times 0.5 .. 6 (a multiple of
+    2^(e-1)); it is exact in FP16 iff 2^(e-1) >= 2^-24 (the smallest
+    subnormal) and 6 x 2^e <= 65504, i.e. e in [-23, 13] (E8M0 bytes 104 ..
+    140).  Bytes 103 and 141 must each hold an inexact product."""
+    w = _all_products(o, 0, list(range(0x7F)))
+    assert np.array_equal(o.fp16_bits_to_f64(o.fp16_bits_of_exact(w)), w)
+    w = _all_products(o, 1, list(range(104, 141)))
+    assert np.array_equal(o.fp16_bits_to_f64(o.fp16_bits_of_exact(w)), w)
+    for byte in (103, 141):
+        with pytest.raises(ValueError):
+            o.fp16_bits_of_exact(_all_products(o, 1, [byte]))
+
+
+def _f16_bits(rows):
+    return np.asarray(rows, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def pin_worked_examples_fp16(o):
+    """The worked examples' activations are small integers, exact in FP16:
+    with FP16 activation bits the reference must give the same hand-derived
+    results as with BF16 bits."""
+    ex = _golden("worked_examples.json")
+    expected = {
+        "nvfp4_2x16": ([[54.0, 2.8125], [0.0, 24.375]], [[54.0, 15.9375], [108.0, 31.875]]),
+        "mxfp4_1x32": ([[19.0]], [[37.0]]),
+    }
+    for key, (y_hand, b_hand) in expected.items():
+        e = ex[key]
+        y, b = o.gemm_reference(_f16_bits(e["A"]), np.array(e["packed_bytes"], dtype=np.uint8),
+                                np.array(e["scale_bytes"], dtype=np.uint8), e["K"], e["fmt"], act="f16")
+        assert y.tolist() == y_hand, key
+        assert b.tolist() == b_hand, key
+        assert o.check_tolerance(_f16_bits(y_hand), y, b, act="f16").all()
+
+
+def pin_tolerance_fp16(o):
+    y_ref = np.array([[1.0, -3.0, 100.0, 0.0]])
+    bound = np.array([[1.0, 3.0, 100.0, 50.0]])
+    assert o.check_tolerance(_f16_bits(y_ref), y_ref, bound, act="f16").all()
+    bad = _f16_bits([[1.02, -3.06, 102.0, 0.2]])
+    assert not o.check_tolerance(bad, y_ref, bound, act="f16").any()
+    # 65520 rounds to Inf in FP16: an overflowed output fails.
+    assert not o.check_tolerance(_f16_bits([[65520.0]]), np.array([[65000.0]]),
+                                 np.array([[65000.0]]), act="f16").any()
+
+
 ALL_PINS = [pin_e2m1_page_list, pin_e4m3_library, pin_e8m0_library, pin_dequant_bruteforce,
             pin_worked_examples, pin_gemm_fsum, pin_multi_group_scales, pin_nibble_order,
-            pin_products_exact_in_bf16, pin_tolerance]
+            pin_products_exact_in_bf16, pin_tolerance, pin_fp16_decode_library,
+            pin_products_exact_in_fp16, pin_worked_examples_fp16, pin_tolerance_fp16]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -279,6 +352,7 @@ class _Mutant:
 _ORIG_UNPACK = O.unpack_codes
 _ORIG_E4M3 = O.e4m3_value
 _ORIG_E2M1 = O.e2m1_value
+_ORIG_FP16 = O.fp16_bits_to_f64
 
 
 def _mut_e2m1_bias2(code):
@@ -305,17 +379,25 @@ def _mut_dequant_group_shift(codes, scales, K, fmt):
     return vals * s
 
 
-def _mut_gemm_transposed(a_bits, codes, scales, K, fmt):
-    y, b = O.gemm_reference(a_bits, codes, scales, K, fmt)
+def _mut_gemm_transposed(a_bits, codes, scales, K, fmt, act="bf16"):
+    y, b = O.gemm_reference(a_bits, codes, scales, K, fmt, act)
     if y.shape[0] == y.shape[1]:
         return y.T, b.T
     return y, b
 
 
-def _mut_gemm_no_abs_bound(a_bits, codes, scales, K, fmt):
-    a = O.bf16_bits_to_f64(a_bits)
+def _mut_gemm_no_abs_bound(a_bits, codes, scales, K, fmt, act="bf16"):
+    a = O.act_bits_to_f64(a_bits, act)
     w = O.dequant_weights(codes, scales, K, fmt)
     return a @ w.T, np.abs(a @ w.T)
+
+
+def _mut_fp16_bias16(bits):
+    return _ORIG_FP16(bits) / 2.0
+
+
+def _mut_gemm_act_ignored(a_bits, codes, scales, K, fmt, act="bf16"):
+    return O.gemm_reference(a_bits, codes, scales, K, fmt)
 
 
 def _mut_sign_dropped(code):
@@ -330,13 +412,15 @@ def _mut_sign_dropped(code):
     ("scale group off by one", {"dequant_weights": _mut_dequant_group_shift}),
     ("output transposed", {"gemm_reference": _mut_gemm_transposed}),
     ("bound without abs", {"gemm_reference": _mut_gemm_no_abs_bound}),
+    ("fp16 read with bias 16", {"fp16_bits_to_f64": _mut_fp16_bias16}),
+    ("fp16 activations read as bf16", {"gemm_reference": _mut_gemm_act_ignored}),
 ])
 def test_planted_mistake_is_caught(name, over):
     # The mutant module re-routes the named function; functions of the real
     # module that call it internally still use the original, so the mutants
     # are rebuilt on top of module-level replacements where needed.
     mod = _Mutant(**over)
-    if "e2m1_value" in over or "unpack_codes" in over or "e4m3_value" in over:
+    if {"e2m1_value", "unpack_codes", "e4m3_value", "fp16_bits_to_f64"} & set(over):
         saved = {k: getattr(O, k) for k in over}
         try:
             for k, v in over.items():

@@ -453,30 +453,41 @@ __global__ __launch_bounds__(256) void reduce_partials(const float* __restrict__
 }
 
 // ----------------------------------------------------------- prefill GEMM
-// Larger m.  A 256-thread workgroup computes a BM (m) x BN (n) tile with its
-// four waves in a WM x WN grid (a wave owns MBW 16-row m-blocks and TNW
-// n-tiles), over a K range (the whole K, or 1/S of it with FP32 partials).
-// Per 128-K chunk c:
-//   issue the activations of chunk c+2 into register set c % 2 and the code
-//   blocks of chunk c+3 into ring slot (c+3) % 4 (scales one 512-K block
-//   ahead), multiply chunk c from LDS buffer c % 2 and ring slot c % 4, write
-//   the activations of chunk c+1 (issued one step earlier) to LDS buffer
-//   (c+1) % 2, barrier (LDS only).
-// Loads are issued in the order they are waited for, so the wait before each
-// LDS write leaves the younger code prefetches in flight.  The activation
-// tile is XOR-swizzled by row in LDS (conflict-free 16-byte writes and
-// fragment reads; the Petit blog, "Mastering the memory hierarchy").
+// Larger m.  A workgroup of four or eight waves computes a BM (m) x BN (n)
+// tile with its waves in a WM x WN grid (a wave owns MBW 16-row m-blocks and
+// TNW n-tiles), over a K range (the whole K, or 1/S of it with FP32
+// partials).  Eight waves run two per SIMD, so one wave's dequant and memory
+// instructions issue while the other's matrix instructions execute.
+// Activations go global -> registers -> LDS (two chunk buffers, XOR-swizzled
+// by row: conflict-free 16-byte writes and fragment reads; the Petit blog,
+// "Mastering the memory hierarchy"); codes go global -> registers through a
+// 4-slot ring, three chunks ahead; scales one 512-K block ahead.
+// Per 128-K chunk c (four MFMA steps i = 0..3), with the activation
+// fragments of each step read from LDS one step ahead:
+//   issue the code blocks of chunk c+3;
+//   steps 0..2 of chunk c, each reading the fragments of the next step;
+//   barrier: every wave is done with LDS buffer c % 2, and the chunk c+1
+//     activations written one chunk earlier are visible;
+//   write the activations of chunk c+2 to buffer c % 2 and issue those of
+//     chunk c+4 (two register sets) or c+3 (one set, for the shapes whose
+//     accumulators leave no room for two) into the freed register set;
+//   step 3 of chunk c, reading step 0 of chunk c+1 from buffer (c+1) % 2.
+// So no fragment read waits on its own step's products, and the one barrier
+// per chunk sits where three steps' products are still in flight.
 template <int FMT, int ACT, int WM, int WN, int MBW, int TNW, bool KTAIL>
-__global__ __launch_bounds__(256) void gemm_prefill(const uint16_t* __restrict__ A, const u32x4* __restrict__ wq,
-                                                   const uint8_t* __restrict__ sq, uint16_t* __restrict__ C,
-                                                   float* __restrict__ P, int M, int N, int K, int KB, int SB, int NT,
-                                                   int S) {
-    static_assert(WM * WN == 4, "four waves");
+__global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __restrict__ A,
+                                                            const u32x4* __restrict__ wq,
+                                                            const uint8_t* __restrict__ sq, uint16_t* __restrict__ C,
+                                                            float* __restrict__ P, int M, int N, int K, int KB,
+                                                            int SB, int NT, int S) {
+    static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
     typedef u32x4 SW;
-    constexpr int BM = WM * MBW * 16;  // m rows per workgroup
-    constexpr int BNT = WN * TNW;      // n-tiles per workgroup
-    constexpr int kBuf = BM * 256;     // one LDS activation buffer (BM x 128 K x 2 B)
-    constexpr int kStage = BM / 16;    // 16-byte activation pieces per thread per chunk
+    constexpr int kThreads = 64 * WM * WN;
+    constexpr int BM = WM * MBW * 16;          // m rows per workgroup
+    constexpr int BNT = WN * TNW;              // n-tiles per workgroup
+    constexpr int kBuf = BM * 256;             // one LDS activation buffer (BM x 128 K x 2 B)
+    constexpr int kStage = BM * 16 / kThreads;  // 16-byte activation pieces per thread per chunk
+    static_assert(kStage * kThreads == BM * 16, "whole pieces per thread");
     constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kBuf];
 
@@ -515,26 +526,32 @@ __global__ __launch_bounds__(256) void gemm_prefill(const uint16_t* __restrict__
     int lds_off[kStage];
 #pragma unroll
     for (int q = 0; q < kStage; ++q) {
-        const int idx = tid + 256 * q;
+        const int idx = tid + kThreads * q;
         const int row = idx >> 4, col = idx & 15;
         aoff[q] = (uint32_t)((m0 + row) * K + col * 8) * 2u;
         lds_off[q] = row * 256 + ((col ^ (row & 15)) << 4);
     }
-    u32x4 st[2][kStage];
+    // Register sets for activations in flight: two (issued two chunks before
+    // they are written to LDS) when the registers leave room (eight waves:
+    // half the pieces per thread; four waves: fewer than 32 accumulator
+    // tiles), else one.
+    constexpr int kSets = (WM * WN == 8 || MBW * TNW < 32) ? 2 : 1;
+    u32x4 st[kSets][kStage];
     auto a_issue = [&](auto set_c, int chunk) {
-        constexpr int SET = decltype(set_c)::value;
+        constexpr int SET = decltype(set_c)::value % kSets;
         chunk = min(chunk, clast);
 #pragma unroll
         for (int q = 0; q < kStage; ++q) {
-            const int k = chunk * kChunkK + (((tid + 256 * q) & 15) * 8);
+            const int k = chunk * kChunkK + (((tid + kThreads * q) & 15) * 8);
             const uint32_t off = aoff[q] + (uint32_t)(chunk * kChunkK) * 2u;
             st[SET][q] = load_a(ra, (!KTAIL || k < K) ? off : kOutOfRange);
         }
     };
-    auto a_store = [&](auto set_c) {
-        constexpr int SET = decltype(set_c)::value;
+    auto a_store = [&](auto set_c, auto buf_c) {
+        constexpr int SET = decltype(set_c)::value % kSets;
+        constexpr int BUF = decltype(buf_c)::value;
 #pragma unroll
-        for (int q = 0; q < kStage; ++q) *reinterpret_cast<u32x4*>(lds_a + SET * kBuf + lds_off[q]) = st[SET][q];
+        for (int q = 0; q < kStage; ++q) *reinterpret_cast<u32x4*>(lds_a + BUF * kBuf + lds_off[q]) = st[SET][q];
     };
     u32x4 wr[4][TNW];
     auto w_issue = [&](auto slot_c, int chunk) {
@@ -549,6 +566,17 @@ __global__ __launch_bounds__(256) void gemm_prefill(const uint16_t* __restrict__
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
+    // this lane's fragments (16-byte column 4 I + j of its rows) of step I
+    // of the chunk in LDS buffer BUF
+    auto read_frags = [&](auto i_c, auto buf_c, u32x4 (&a)[MBW]) {
+        constexpr int I = decltype(i_c)::value;
+        constexpr int BUF = decltype(buf_c)::value;
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+            const int row = wm * MBW * 16 + mb * 16 + r;
+            a[mb] = *reinterpret_cast<const u32x4*>(lds_a + BUF * kBuf + row * 256 + (((4 * I + j) ^ (row & 15)) << 4));
+        }
+    };
 
     f32x4 acc[TNW][MBW];
 #pragma unroll
@@ -556,53 +584,84 @@ __global__ __launch_bounds__(256) void gemm_prefill(const uint16_t* __restrict__
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // multiply chunk (position T in its 512-K block) from LDS buffer BUF.
-    // The dequant of tile tt+1 is placed before the products of tile tt and
-    // the scheduler is asked to alternate one matrix instruction with two
-    // vector instructions, so the dequant runs while the matrix core works.
-    auto compute = [&](auto t_c, auto buf_c, const SW (&sc)[TNW]) {
+    // Products of step I of chunk position T with fragments a.  The dequant
+    // of tile tt+1 is placed before the products of tile tt and the scheduler
+    // is asked to alternate one matrix instruction with two vector
+    // instructions, so the dequant runs while the matrix core works.
+    auto mma = [&](auto t_c, auto i_c, const u32x4 (&a)[MBW], const SW (&sc)[TNW]) {
         constexpr int T = decltype(t_c)::value;
-        constexpr int BUF = decltype(buf_c)::value;
-        const uint8_t* base = lds_a + BUF * kBuf;
-        auto step = [&](auto ii) {
-            constexpr int I = decltype(ii)::value;
-            u32x4 a[MBW];
+        constexpr int I = decltype(i_c)::value;
+        u32x4 wf[TNW];
+        wf[0] = dequant_step<FMT, T, I, ACT>(wr[T][0], sc[0]);
 #pragma unroll
-            for (int mb = 0; mb < MBW; ++mb) {
-                const int row = wm * MBW * 16 + mb * 16 + r;
-                const int col = 4 * I + j;
-                a[mb] = *reinterpret_cast<const u32x4*>(base + row * 256 + ((col ^ (row & 15)) << 4));
-            }
-            u32x4 wf[TNW];
-            wf[0] = dequant_step<FMT, T, I, ACT>(wr[T][0], sc[0]);
+        for (int tt = 0; tt < TNW; ++tt) {
+            if (tt + 1 < TNW) wf[tt + 1] = dequant_step<FMT, T, I, ACT>(wr[T][tt + 1], sc[tt + 1]);
 #pragma unroll
-            for (int tt = 0; tt < TNW; ++tt) {
-                if (tt + 1 < TNW) wf[tt + 1] = dequant_step<FMT, T, I, ACT>(wr[T][tt + 1], sc[tt + 1]);
-#pragma unroll
-                for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = mfma<ACT>(wf[tt], a[mb], acc[tt][mb]);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, MBW, 0);  // fragment reads first
-#pragma unroll
-            for (int q = 0; q < MBW * TNW; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
-            }
-        };
-        step(std::integral_constant<int, 0>{});
-        step(std::integral_constant<int, 1>{});
-        step(std::integral_constant<int, 2>{});
-        step(std::integral_constant<int, 3>{});
+            for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = mfma<ACT>(wf[tt], a[mb], acc[tt][mb]);
+        }
     };
-    // step for chunk c = base + T (T = c % 4; c % 2 == T % 2)
+    auto interleave = [] {
+        __builtin_amdgcn_sched_group_barrier(0x100, MBW, 0);  // next step's fragment reads first
+#pragma unroll
+        for (int q = 0; q < MBW * TNW; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // Four-wave shapes read each step's fragments one step ahead (two
+    // fragment sets); eight-wave shapes have no registers to spare for that
+    // and rely on the other wave of their SIMD to cover the LDS latency.
+    constexpr bool kPrefetch = WM * WN == 4;
+    u32x4 fa[MBW], fb[kPrefetch ? MBW : 1];
+    // chunk c = base + T (T = c % 4; c % 2 == T % 2); fa holds step 0's
+    // fragments when prefetching
     auto pstep = [&](auto t_c, int base, const SW (&cur)[TNW]) {
         constexpr int T = decltype(t_c)::value;
-        a_issue(std::integral_constant<int, T % 2>{}, base + T + 2);
+        using B = std::integral_constant<int, T % 2>;
         w_issue(std::integral_constant<int, (T + 3) % 4>{}, base + T + 3);
         __builtin_amdgcn_sched_barrier(0);
-        compute(t_c, std::integral_constant<int, T % 2>{}, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        a_store(std::integral_constant<int, (T + 1) % 2>{});
-        lds_barrier();
+        if constexpr (!kPrefetch) {
+            auto one = [&](auto i_c) {
+                read_frags(i_c, B{}, fa);
+                mma(t_c, i_c, fa, cur);
+                interleave();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            one(I0{});
+            one(I1{});
+            one(I2{});
+            one(I3{});
+            lds_barrier();
+            a_store(B{}, B{});
+            a_issue(B{}, base + T + 2 + kSets);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            using NB = std::integral_constant<int, (T + 1) % 2>;
+            read_frags(I1{}, B{}, fb);
+            mma(t_c, I0{}, fa, cur);
+            interleave();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(I2{}, B{}, fa);
+            mma(t_c, I1{}, fb, cur);
+            interleave();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(I3{}, B{}, fb);
+            mma(t_c, I2{}, fa, cur);
+            interleave();
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            a_store(B{}, B{});
+            a_issue(B{}, base + T + 2 + kSets);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(I0{}, NB{}, fa);
+            mma(t_c, I3{}, fb, cur);
+            interleave();
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     SW sa[TNW], sbs[TNW];
     auto block = [&](int sbx, const SW (&cur)[TNW], SW (&nxt)[TNW]) {
@@ -610,21 +669,28 @@ __global__ __launch_bounds__(256) void gemm_prefill(const uint16_t* __restrict__
         const int nsb = min(sbx + 1, sb1 - 1);
 #pragma unroll
         for (int tt = 0; tt < TNW; ++tt) nxt[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
-        pstep(std::integral_constant<int, 0>{}, base, cur);
-        pstep(std::integral_constant<int, 1>{}, base, cur);
-        pstep(std::integral_constant<int, 2>{}, base, cur);
-        pstep(std::integral_constant<int, 3>{}, base, cur);
+        pstep(I0{}, base, cur);
+        pstep(I1{}, base, cur);
+        pstep(I2{}, base, cur);
+        pstep(I3{}, base, cur);
     };
 
+    // prologue: chunks c0, c0+1 into LDS buffers 0, 1; chunks c0+2, c0+3 in
+    // flight in register sets 0, 1; code blocks c0 .. c0+2 in flight.
 #pragma unroll
     for (int tt = 0; tt < TNW; ++tt) sa[tt] = load_scale_block<FMT>(rs[tt], soff, sb0);
-    a_issue(std::integral_constant<int, 0>{}, c0);
-    w_issue(std::integral_constant<int, 0>{}, c0);
-    w_issue(std::integral_constant<int, 1>{}, c0 + 1);
-    w_issue(std::integral_constant<int, 2>{}, c0 + 2);
-    a_issue(std::integral_constant<int, 1>{}, c0 + 1);
-    a_store(std::integral_constant<int, 0>{});
+    a_issue(I0{}, c0);
+    if constexpr (kSets == 2) a_issue(I1{}, c0 + 1);
+    w_issue(I0{}, c0);
+    w_issue(I1{}, c0 + 1);
+    w_issue(I2{}, c0 + 2);
+    a_store(I0{}, I0{});
+    if constexpr (kSets == 1) a_issue(I1{}, c0 + 1);
+    a_store(I1{}, I1{});
+    a_issue(I0{}, c0 + 2);
+    if constexpr (kSets == 2) a_issue(I1{}, c0 + 3);
     lds_barrier();
+    if constexpr (kPrefetch) read_frags(I0{}, I0{}, fa);
     int sb = sb0;
     for (; sb + 1 < sb1; sb += 2) {
         block(sb, sa, sbs);

@@ -23,6 +23,8 @@ Printed as the last stdout line, one JSON object:
                hash to the value they were measured on
   prefill      the same four layers at m = 256: TFLOP/s against the 2.5
                PFLOP/s dense BF16 matrix-core peak
+  fp16         the same decode step and prefill with FP16 activations and
+               output (fp4_gemm_f16; FP16 matrix-core peak 2.5 PFLOP/s)
   cpu_baseline the CPU oracle (float64 NumPy) timed on a bounded sample
 """
 
@@ -73,6 +75,7 @@ def parse():
     ap.add_argument("--prefill-launches", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp16", action="store_true", help="skip the FP16-activation decode and prefill lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (known bytes for HBM counter scaling)")
     return ap.parse_args()
@@ -94,20 +97,20 @@ class Layer:
         self.sq = [sq_d] + [sq_d.clone() for _ in range(self.R - 1)]
 
 
-def make_call(F, torch, layer, A, C, r, ws):
-    """Pre-marshalled fp4_gemm call on torch's current stream."""
+def make_call(F, torch, layer, A, C, r, ws, entry="fp4_gemm"):
+    """Pre-marshalled fp4_gemm (or fp4_gemm_f16) call on torch's current stream."""
     lib = F.lib()
     stream = F._c_vp(torch.cuda.current_stream().cuda_stream)
     m = A.shape[0]
     ws_bytes = ws.numel() if ws is not None else 0
     args = (F._dev_ptr(A), F._dev_ptr(layer.wq[r]), F._dev_ptr(layer.sq[r]), F._dev_ptr(C), m, layer.N, layer.K,
             layer.fmt, F._dev_ptr(ws), ws_bytes, stream)
-    fn = lib.fp4_gemm
+    fn = getattr(lib, entry)
 
     def call():
         st = fn(*args)
         if st:
-            F._check(st, "fp4_gemm")
+            F._check(st, entry)
     return call
 
 
@@ -137,6 +140,57 @@ def cpu_baseline(decode_layers_probs):
                       f"matmul, mean of {reps} runs ({t:.2f} s each); elementwise dequant runs on one thread, "
                       f"the matmul on {blas_threads} BLAS threads",
             "seconds_per_run": round(t, 3)}
+
+
+def timed(calls_fn, n):
+    """Mean microseconds per call of n back-to-back calls (HIP events on the
+    current stream)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(n):
+        calls_fn(s)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
+
+
+def fp16_lines(args, F, torch, layers, A_bf16, WS, dev, m):
+    """Decode step (m = 16) and prefill (m = 256) with FP16 activations: the
+    BF16 activations converted to FP16, the same packed weights, rotation and
+    protocol as the BF16 lines."""
+    A = [a.to(torch.float16) for a in A_bf16]
+    C = [torch.empty((m, l.N), dtype=torch.float16, device=dev) for l in layers]
+    calls = [[make_call(F, torch, l, A[i], C[i], r, WS[i], "fp4_gemm_f16") for r in range(l.R)]
+             for i, l in enumerate(layers)]
+
+    def step(s):
+        for i, l in enumerate(layers):
+            calls[i][s % l.R]()
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    us_step = timed(step, args.steps)
+    bytes_step = sum(algorithmic_bytes(m, l.N, l.K, l.G) for l in layers)
+    gbs = bytes_step / (us_step * 1e-6) / 1e9
+    out = {"decode_step_us": round(us_step, 2), "decode_GB/s": round(gbs, 1),
+           "decode_frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    if not args.no_prefill:
+        mp = 256
+        rng = np.random.Generator(np.random.PCG64(2_000_000))
+        tot_f, tot_t = 0.0, 0.0
+        for l in layers:
+            a = torch.from_numpy(rng.standard_normal((mp, l.K), dtype=np.float32)).to(torch.float16).to(dev)
+            c = torch.empty((mp, l.N), dtype=torch.float16, device=dev)
+            ws = F.new_workspace(mp, l.N, l.K, l.fmt, device=dev)
+            pc = [make_call(F, torch, l, a, c, r, ws, "fp4_gemm_f16") for r in range(l.R)]
+            for s in range(5):
+                pc[s % l.R]()
+            tot_t += timed(lambda s: pc[s % l.R](), args.prefill_launches)
+            tot_f += 2.0 * mp * l.N * l.K
+        out["prefill_TFLOP/s"] = round(tot_f / tot_t / 1e6, 1)
+        out["prefill_frac_mfma"] = round(tot_f / tot_t / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)
+    return out
 
 
 def main():
@@ -254,6 +308,12 @@ def main():
                    "note": "weights of the decode layers; A drawn N(0,1) in BF16 with its own seed"}
         log(f"prefill m=256: {prefill['TFLOP/s']} TFLOP/s")
 
+    fp16 = None
+    if not args.no_fp16:
+        fp16 = fp16_lines(args, F, torch, layers, A, WS, dev, m)
+        log(f"fp16: decode step {fp16['decode_step_us']} us -> {fp16['decode_GB/s']} GB/s; "
+            f"prefill m=256 {fp16['prefill_TFLOP/s']} TFLOP/s")
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(probs)
 
     out = {
@@ -280,6 +340,7 @@ def main():
                      "traffic": measured_traffic()},
         "layers": per_layer,
         "prefill": prefill,
+        "fp16": fp16,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

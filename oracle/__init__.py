@@ -29,3 +29,4 @@ from .fp4_oracle import (  # noqa: F401
     scale_value,
     unpack_codes,
 )
+from .moe_oracle import moe_reference  # noqa: F401,E402

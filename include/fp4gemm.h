@@ -152,6 +152,36 @@ int fp4_dequant(const void* wq, const void* sq, void* W_bf16, int64_t N, int64_t
 int fp4_dequant_f16(const void* wq, const void* sq, void* W_f16, int64_t N, int64_t K, int format,
                     void* stream);
 
+/* Grouped mixture-of-experts GEMM with BF16 activations (the petit-kernel
+ * page, "Features": fused MoE kernels for BF16 and MXFP4 workloads; both FP4
+ * formats are accepted).  For expert e = 0 .. E-1 and every assignment id
+ * in sorted_ids[expert_offsets[e] .. expert_offsets[e+1]):
+ *     C[id][:] = w(id) * A[id / a_div] . dequant(W_e)^T
+ * with w(id) = topk_weights[id] (FP32, multiplied before rounding) or 1 when
+ * topk_weights is NULL.  a_div is the number of experts per token when A
+ * holds one row per token (gate/up projection), 1 when A holds one row per
+ * assignment (down projection).
+ *   A              device, BF16 [a_rows][K] row-major
+ *   wq, sq         device, E experts' packed weights back to back, each
+ *                  exactly the fp4_repack_size(N, K, format) bytes of one
+ *                  N x K matrix (expert e at e * wq_bytes / e * sq_bytes)
+ *   sorted_ids     device, int32 [P], assignment ids grouped by expert; each
+ *                  id at most once (a repeated id is a write race)
+ *   expert_offsets device, int32 [E + 1], non-decreasing, from 0 to P
+ *                  (values are clamped to [0, P])
+ *   topk_weights   device, FP32 [out_rows] indexed by id, or NULL
+ *   C              device, BF16 [out_rows][N]; only the rows listed in
+ *                  sorted_ids are written; ids outside [0, out_rows) are
+ *                  skipped, rows id / a_div >= a_rows read as zeros
+ * A, wq, sq and C 16-byte aligned, the int32 / FP32 arrays 4-byte aligned.
+ * P == 0 is a no-op.  No workspace (no K split).  Asynchronous on `stream`;
+ * deterministic.  Errors as for fp4_gemm; FP4_ERR_SHAPE also for E outside
+ * 1 .. 4096, P > 2^24, a_div < 1 or a grid that would need more than 65535
+ * row blocks (P / 16 + E). */
+int fp4_moe_gemm(const void* A, const void* wq, const void* sq, const int32_t* sorted_ids,
+                 const int32_t* expert_offsets, const float* topk_weights, void* C, int64_t a_rows, int64_t a_div,
+                 int64_t out_rows, int64_t P, int64_t E, int64_t N, int64_t K, int format, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libfp4gemm.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["repack.cpp", "fp4gemm.hip", "decode_bf16.hip", "decode_f16.hip", "prefill_bf16.hip", "prefill_f16.hip"]
+SOURCES = ["repack.cpp", "fp4gemm.hip", "decode_bf16.hip", "decode_f16.hip", "prefill_bf16.hip", "prefill_f16.hip",
+           "moe_bf16.hip"]
 HEADERS = ["layout.h", "kernels.h", "dispatch.h", "decode_inst.inc", "prefill_inst.inc",
            os.path.join("..", "..", "include", "fp4gemm.h")]
 

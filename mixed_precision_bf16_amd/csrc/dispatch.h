@@ -20,6 +20,22 @@ struct PrefillShape {
     int wm, wn, mbw, tnw, s;
 };
 
+// Grouped MoE problem (see the MoE routing note in kernels.h): expert e owns
+// the packed weights at wq + e * w_stride / sq + e * s_stride and the
+// assignment ids ids[offsets[e] .. offsets[e+1]); assignment id reads
+// activation row id / a_div and writes output row id, scaled by topw[id]
+// when topw is not null.
+struct MoeArgs {
+    const int32_t* ids;
+    const int32_t* offsets;
+    const float* topw;
+    int E, P;      // experts; entries of ids
+    int a_div;     // activation row of an assignment = id / a_div
+    int a_rows;    // rows of A
+    int out_rows;  // rows of C; ids outside [0, out_rows) are skipped
+    int64_t w_stride, s_stride;
+};
+
 // Compiled decode shapes: X(MB, TN, NWN, NWK).
 #define FP4_DECODE_SHAPES(X)                                                                         \
     X(1, 1, 4, 1) X(1, 2, 4, 1) X(1, 1, 4, 2) X(1, 2, 4, 2) X(1, 1, 4, 4) X(1, 2, 1, 4) X(1, 2, 1, 1)  \
@@ -42,5 +58,12 @@ bool launch_prefill_bf16(int fmt, const PrefillShape& t, const void* A, const vo
                          float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s);
 bool launch_prefill_f16(int fmt, const PrefillShape& t, const void* A, const void* wq, const void* sq, void* C,
                         float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s);
+
+// Compiled MoE shapes (BF16 activations): X(MB, TN, NWN); one K group, no K
+// split.  `items` bounds the number of row blocks (grid height).
+#define FP4_MOE_SHAPES(X) \
+    X(1, 1, 2) X(1, 1, 4) X(1, 1, 8) X(1, 2, 8) X(2, 1, 4) X(2, 1, 8) X(2, 2, 8) X(4, 1, 4) X(4, 1, 8) X(4, 2, 8)
+bool launch_moe_bf16(int fmt, int MB, int tn, int nwn, const void* A, const void* wq, const void* sq, void* C,
+                     const MoeArgs& moe, int N, int K, int KB, int SB, int NT, int items, hipStream_t s);
 
 }  // namespace fp4

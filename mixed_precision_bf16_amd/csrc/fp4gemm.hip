@@ -261,9 +261,71 @@ static int dequant_impl(int act, const void* wq, const void* sq, void* W, int64_
     return launch_status();
 }
 
+// Grouped MoE GEMM.  The row counts per expert live on the device, so the
+// grid is sized for the worst case (sum over experts of ceil(rows / block)
+// <= P / block + E row blocks) and surplus workgroups exit at once.  Row
+// block: 16 rows while the mean rows per expert is at most 16, else 32 or
+// 64.  Tiles per workgroup: the most (16, 8, 4, 2) that still give about
+// 1024 workgroups over the likely row blocks (min(P, E) for one-row-block
+// experts): an active expert's weights are streamed once per row block, so
+// the grid should cover the CUs several times over.
+static int moe_impl(const void* A, const void* wq, const void* sq, const int32_t* ids, const int32_t* offsets,
+                    const float* topw, void* C, int64_t a_rows, int64_t a_div, int64_t out_rows, int64_t P,
+                    int64_t E, int64_t N, int64_t K, int format, void* stream) {
+    int st = fp4_check_weight_shape(N, K, format);
+    if (st != FP4_OK) return st;
+    if (E < 1 || E > 4096 || P < 0 || P > (int64_t(1) << 24) || a_div < 1 || a_rows < 1 || out_rows < 1 ||
+        out_rows > (int64_t(1) << 24))
+        return FP4_ERR_SHAPE;
+    if (P == 0) return FP4_OK;
+    if (!A || !wq || !sq || !ids || !offsets || !C) return FP4_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(wq) | reinterpret_cast<uintptr_t>(sq) |
+         reinterpret_cast<uintptr_t>(C)) & 15)
+        return FP4_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(ids) | reinterpret_cast<uintptr_t>(offsets) |
+         reinterpret_cast<uintptr_t>(topw)) & 3)
+        return FP4_ERR_SHAPE;
+    if (round_up(a_rows, 64) * K * 2 >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
+    const int64_t Np = padded_n(N), Kp = padded_k(K);
+    const int KB = int(Kp / kChunkK), SB = int(Kp / kScaleBlockK), NT = int(Np / kTileN);
+    const int64_t G = format == FP4_NVFP4 ? 16 : 32;
+    const int64_t w_stride = Np * Kp / 2, s_stride = Np * Kp / G;
+    const int64_t mean_rows = (P + E - 1) / E;
+    const int MB = mean_rows <= 16 ? 1 : (mean_rows <= 32 ? 2 : 4);
+    const int64_t rows = 16 * MB;
+    const int64_t items = (P + rows - 1) / rows + E;
+    if (items > 65535) return FP4_ERR_SHAPE;
+    st = check_device();
+    if (st != FP4_OK) return st;
+    const int64_t likely = std::max<int64_t>(1, std::min(P, E));
+    static const int kTw[4][3] = {{16, 2, 8}, {8, 1, 8}, {4, 1, 4}, {2, 1, 2}};
+    int pick = 3;
+    for (int i = 0; i < 4; ++i)
+        if (likely * ((NT + kTw[i][0] - 1) / kTw[i][0]) >= 1024) {
+            pick = i;
+            break;
+        }
+    int tn = kTw[pick][1], nwn = kTw[pick][2];
+    if (MB > 1 && tn * nwn == 2) nwn = 4;  // the two-tile shape is compiled for 16-row blocks only
+    MoeArgs moe{ids, offsets, topw, int(E), int(P), int(a_div), int(a_rows), int(out_rows), w_stride, s_stride};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (!launch_moe_bf16(format, MB, tn, nwn, A, wq, sq, C, moe, int(N), int(K), KB, SB, NT, int(items), s))
+        return FP4_ERR_SHAPE;
+    return launch_status();
+}
+
 }  // namespace fp4
 
 using namespace fp4;
+
+extern "C" int fp4_moe_gemm(const void* A, const void* wq, const void* sq, const int32_t* sorted_ids,
+                            const int32_t* expert_offsets, const float* topk_weights, void* C, int64_t a_rows,
+                            int64_t a_div, int64_t out_rows, int64_t P, int64_t E, int64_t N, int64_t K, int format,
+                            void* stream) {
+    return moe_impl(A, wq, sq, sorted_ids, expert_offsets, topk_weights, C, a_rows, a_div, out_rows, P, E, N, K,
+                    format, stream);
+}
 
 extern "C" int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int format, size_t* bytes) {
     int st = fp4_check_weight_shape(N, K, format);

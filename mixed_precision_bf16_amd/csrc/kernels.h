@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "../../include/fp4gemm.h"
+#include "dispatch.h"
 #include "layout.h"
 
 namespace fp4 {
@@ -202,6 +203,53 @@ __device__ __forceinline__ u32x4 load_scale_block(__amdgpu_buffer_rsrc_t r, int 
     return __builtin_amdgcn_raw_buffer_load_b128(r, soff_lane, sb * scale_block_bytes<FMT>(), kLoadStream);
 }
 
+// ------------------------------------------------------------ MoE routing
+// Grouped mixture-of-experts GEMM (the petit-kernel page, "Features": fused
+// MoE kernels for BF16 x MXFP4): expert e owns the packed weights at
+// wq + e * w_stride / sq + e * s_stride (each the dense layout of N x K) and
+// the assignment ids sorted_ids[offsets[e] .. offsets[e+1]); assignment id
+// reads activation row id / a_div and writes output row id, scaled by
+// topw[id] when topw is given.
+// (MoeArgs is declared in dispatch.h, shared with the host.)
+
+// Row block `item` of the grouped problem: blocks of `rows` assignments are
+// numbered expert by expert.  Returns the expert (or -1 past the last
+// block) and its first assignment and row count.  Every lane of the wave
+// computes the same result: lane x of a 64-expert window counts the blocks
+// of expert base + x and a wave prefix sum finds the owner.
+__device__ __forceinline__ int moe_find_block(const MoeArgs& moe, int item, int rows, int& first_row, int& nrows) {
+    const int lane = threadIdx.x & 63;
+    int before = 0;
+    for (int base = 0; base < moe.E; base += 64) {
+        const int x = base + lane;
+        int nb = 0, o0 = 0, o1 = 0;
+        if (x < moe.E) {
+            o0 = min(max(moe.offsets[x], 0), moe.P);
+            o1 = min(max(moe.offsets[x + 1], o0), moe.P);
+            nb = (o1 - o0 + rows - 1) / rows;
+        }
+        int inc = nb;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(inc, d, 64);
+            if (lane >= d) inc += t;
+        }
+        const int start = before + inc - nb;
+        const unsigned long long own = __ballot(x < moe.E && item >= start && item < start + nb);
+        if (own) {
+            const int src = __ffsll(own) - 1;
+            const int e = __shfl(x, src, 64);
+            const int blk = item - __shfl(start, src, 64);
+            const int o0s = __shfl(o0, src, 64), o1s = __shfl(o1, src, 64);
+            first_row = __builtin_amdgcn_readfirstlane(o0s + blk * rows);
+            nrows = __builtin_amdgcn_readfirstlane(min(rows, o1s - o0s - blk * rows));
+            return __builtin_amdgcn_readfirstlane(e);
+        }
+        before += __shfl(inc, 63, 64);
+    }
+    return -1;
+}
+
 // ------------------------------------------------------------ decode GEMM
 // Small m (<= 16*MB) with the activations shared through LDS.  A workgroup has
 // NWK groups of NWN waves.  The waves of one group cover the same K range and
@@ -223,12 +271,17 @@ __device__ __forceinline__ u32x4 load_scale_block(__amdgpu_buffer_rsrc_t r, int 
 // x-1 used.  One barrier per block (LDS only: the prefetches stay in flight)
 // separates those writes from the reads of block x+1 and the reads of block
 // x-1 from the writes.
-template <int FMT, int ACT, int MB, int TN, int NWN, int NWK>
+//
+// MOE: the same kernel over one row block of one expert (MoeArgs above):
+// blockIdx.y numbers the row blocks, the activation rows are gathered by
+// assignment id and the output rows scattered by it; no K split.
+template <int FMT, int ACT, int MB, int TN, int NWN, int NWK, bool MOE = false>
 __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __restrict__ A,
                                                              const u32x4* __restrict__ wq,
                                                              const uint8_t* __restrict__ sq,
                                                              uint16_t* __restrict__ C, float* __restrict__ P, int M,
-                                                             int N, int K, int KB, int SB, int NT, int S) {
+                                                             int N, int K, int KB, int SB, int NT, int S,
+                                                             MoeArgs moe = MoeArgs{}) {
     typedef u32x4 SW;
     constexpr int kRows = 16 * MB;  // activation rows; one 1 KiB load per row per block
     // Activation load instructions per wave per block.  When NWN does not
@@ -247,6 +300,15 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
     const int ks = blockIdx.x % S, grp = blockIdx.x / S;
     const int tile0 = grp * (TN * NWN) + wn * TN;
     const int soff = scale_lane_offset<FMT>(r, j);
+    int row0 = 0;  // MOE: first entry of ids in this row block
+    if constexpr (MOE) {
+        int nrows = 0;
+        const int e = moe_find_block(moe, blockIdx.y, kRows, row0, nrows);
+        if (e < 0) return;  // whole workgroup, before any barrier
+        M = nrows;
+        wq = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(wq) + (size_t)e * moe.w_stride);
+        sq += (size_t)e * moe.s_stride;
+    }
 
     // K range of the workgroup and of this wave's group, in 512-K scale blocks.
     // Every group runs nblk blocks so that all waves meet at every barrier; a
@@ -259,7 +321,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
     const int sbmax = own > 0 ? sb1 - 1 : wsb0;         // last block this group may read
     const int cmax = own > 0 ? 4 * sb1 - 1 : 4 * wsb0;  // last chunk this group may read
 
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(M * K * 2));
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)((MOE ? moe.a_rows : M) * K * 2));
     __amdgpu_buffer_rsrc_t rw[TN], rs[TN];
 #pragma unroll
     for (int tt = 0; tt < TN; ++tt) {
@@ -288,6 +350,12 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
         const int row = min(wn + NWN * u, kRows - 1);
         alive[u] = row < M;
         aoff[u] = (uint32_t)(row * K + 8 * lane) * 2u;
+        if constexpr (MOE) {
+            // gathered row; an id outside [0, a_div * a_rows) reads zeros
+            const int id = alive[u] ? moe.ids[row0 + row] : 0;
+            const bool in_a = id >= 0 && id / moe.a_div < moe.a_rows;
+            aoff[u] = in_a ? (uint32_t)((id / moe.a_div) * K + 8 * lane) * 2u : kOutOfRange;
+        }
         ldst[u] = a_base + ((row >> 4) * 64 + ((row & 15) ^ a_oct)) * 16;
     }
     uint8_t* const ring = lds_a + wk * 2 * kBlk;
@@ -410,6 +478,20 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                     acc[tt][mb] += red[((((g - 1) * NWN + wn) * TN + tt) * MB + mb) * kLanes + lane];
+    }
+    if constexpr (MOE) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = mb * 16 + r;
+            if (m >= M) continue;
+            const int id = moe.ids[row0 + m];
+            if (id < 0 || id >= moe.out_rows) continue;
+            const float w = moe.topw ? moe.topw[id] : 1.0f;
+#pragma unroll
+            for (int tt = 0; tt < TN; ++tt) store_frag<ACT>(C, acc[tt][mb] * w, id, (tile0 + tt) * kTileN + 4 * j,
+                                                            moe.out_rows, N);
+        }
+        return;
     }
 #pragma unroll
     for (int tt = 0; tt < TN; ++tt)

@@ -37,6 +37,8 @@ _SIGNATURES = {
                                     _c_sz, _c_vp]),
     "fp4_dequant": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
     "fp4_dequant_f16": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
+    "fp4_moe_gemm": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                    _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
 }
 
 STATUS = {0: "FP4_OK", 1: "FP4_ERR_NULL", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_FORMAT", 4: "FP4_ERR_VALUE",
@@ -201,3 +203,36 @@ def upload(wq: np.ndarray, sq: np.ndarray, device="cuda"):
     import torch
     return (torch.from_numpy(np.ascontiguousarray(wq)).to(device),
             torch.from_numpy(np.ascontiguousarray(sq)).to(device))
+
+
+def moe_gemm(A, wq, sq, sorted_ids, expert_offsets, N: int, K: int, fmt: int, E: int, a_div: int, out_rows: int,
+             topk_weights=None, out=None, stream=None):
+    """Grouped MoE GEMM (fp4_moe_gemm): for each expert e and assignment id in
+    sorted_ids[expert_offsets[e]:expert_offsets[e+1]],
+    out[id] = w[id] * A[id // a_div] . dequant(W_e)^T.  wq / sq hold the E
+    experts' packed weights back to back (each repack_size(N, K, fmt)).  Rows
+    of out not listed in sorted_ids are left as they were."""
+    import torch
+    if A.dtype != torch.bfloat16 or A.dim() != 2 or not A.is_cuda or not A.is_contiguous() or A.shape[1] != K:
+        raise ValueError("A must be a contiguous bfloat16 CUDA tensor [a_rows][K]")
+    nw, ns = repack_size(N, K, fmt)
+    for t, n in ((wq, nw), (sq, ns)):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.numel() != E * n:
+            raise ValueError("wq / sq must be contiguous uint8 CUDA tensors holding E packed experts")
+    for t, dt in ((sorted_ids, torch.int32), (expert_offsets, torch.int32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError("sorted_ids / expert_offsets must be contiguous int32 CUDA vectors")
+    if expert_offsets.numel() != E + 1:
+        raise ValueError("expert_offsets must have E + 1 entries")
+    if topk_weights is not None and (topk_weights.dtype != torch.float32 or not topk_weights.is_cuda
+                                     or not topk_weights.is_contiguous() or topk_weights.numel() != out_rows):
+        raise ValueError("topk_weights must be a contiguous float32 CUDA vector of out_rows entries")
+    if out is None:
+        out = torch.zeros((out_rows, N), dtype=torch.bfloat16, device=A.device)
+    elif out.shape != (out_rows, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor [out_rows][N]")
+    _check(lib().fp4_moe_gemm(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(sorted_ids), _dev_ptr(expert_offsets),
+                              _dev_ptr(topk_weights), _dev_ptr(out), A.shape[0], a_div, out_rows,
+                              sorted_ids.numel(), E, N, K, fmt, _stream_handle(stream)), "fp4_moe_gemm")
+    return out
+

@@ -182,3 +182,67 @@ def make_random(m: int, N: int, K: int, fmt: int, seed: int, *,
     a = rng.standard_normal(size=(m, K), dtype=np.float32) * np.float32(a_scale)
     a_bits = _act_bits_of(a, act)
     return Problem(f"rand_m{m}_N{N}_K{K}_f{fmt}_{act}", m, N, K, fmt, a_bits, codes, scales, seed, act)
+
+
+@dataclass
+class MoeProblem:
+    """Grouped MoE instance: A [a_rows][K] BF16 bits, expert codes [E][N][K/2]
+    and scales [E][N][K/G], assignment ids grouped by expert (sorted_ids,
+    offsets [E+1]), routing weights per assignment id (or None)."""
+    name: str
+    T: int
+    topk: int
+    E: int
+    N: int
+    K: int
+    fmt: int
+    a_div: int
+    a_bits: np.ndarray
+    codes: np.ndarray
+    scales: np.ndarray
+    sorted_ids: np.ndarray
+    offsets: np.ndarray
+    topw: np.ndarray | None
+    seed: int
+
+    @property
+    def out_rows(self) -> int:
+        return self.T * self.topk
+
+    @property
+    def a_rows(self) -> int:
+        return self.a_bits.shape[0]
+
+
+def make_moe(T: int, topk: int, E: int, N: int, K: int, fmt: int, seed: int, *, per_assignment_a: bool = False,
+             with_weights: bool = True, skew: float = 0.0) -> MoeProblem:
+    """Seeded synthetic MoE routing and weights.  Each token picks topk
+    distinct experts, uniformly (skew = 0) or with probability proportional
+    to (rank + 1)^-skew over a random expert order (skew > 0 makes a few
+    experts hold many rows and leaves others empty); assignment id =
+    token * topk + slot.  Routing weights are uniform in [0, 1) rounded to
+    FP32.  A holds one row per token (a_div = topk) or, with
+    per_assignment_a, one row per assignment (a_div = 1).  Codes, scales and
+    activations follow the dense generators' distributions.  Draw order:
+    routing -> weights -> codes -> scales -> A."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if skew > 0:
+        p = (np.arange(E) + 1.0) ** -skew
+        p = p[np.argsort(rng.permutation(E))] / p.sum()
+    else:
+        p = None
+    route = np.stack([rng.choice(E, size=topk, replace=False, p=p) for _ in range(T)])   # [T][topk]
+    topw = rng.random(size=T * topk).astype(np.float32) if with_weights else None
+    ids = np.arange(T * topk, dtype=np.int64)
+    expert_of = route.reshape(-1)
+    order = np.argsort(expert_of, kind="stable")
+    sorted_ids = ids[order].astype(np.int32)
+    counts = np.bincount(expert_of, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    codes = np.stack([_draw_codes(rng, N, K) for _ in range(E)])
+    scales = np.stack([_draw_scales(rng, N, K, fmt) for _ in range(E)])
+    a_rows = T * topk if per_assignment_a else T
+    a_bits = _draw_a(rng, a_rows, K)
+    return MoeProblem(f"moe_T{T}_k{topk}_E{E}_N{N}_K{K}_f{fmt}", T, topk, E, N, K, fmt,
+                      1 if per_assignment_a else topk, a_bits, codes, scales, sorted_ids, offsets, topw, seed)
+

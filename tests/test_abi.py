@@ -178,6 +178,33 @@ def test_gemm_argument_errors_before_any_hip_call():
     assert lib.fp4_gemm_workspace_size(16, 64, 64, 0, ctypes.byref(sz)) == 0
 
 
+def test_moe_argument_errors_before_any_hip_call():
+    lib = F.lib()
+    d = ctypes.c_void_p(16)
+    z = ctypes.c_void_p(0)
+
+    def moe(A=d, wq=d, sq=d, ids=d, off=d, tw=z, C=d, a_rows=16, a_div=4, out_rows=64, P=64, E=8, N=64, K=64,
+            fmt=0):
+        return lib.fp4_moe_gemm(A, wq, sq, ids, off, tw, C, a_rows, a_div, out_rows, P, E, N, K, fmt, None)
+    assert moe(fmt=7) == 3
+    assert moe(K=24) == 2
+    assert moe(E=0) == 2 and moe(E=5000) == 2
+    assert moe(a_div=0) == 2 and moe(a_rows=0) == 2 and moe(out_rows=0) == 2
+    assert moe(P=-1) == 2 and moe(P=(1 << 24) + 1) == 2
+    # P = 0 is a no-op, even with null pointers
+    assert moe(A=z, wq=z, sq=z, ids=z, off=z, C=z, P=0) == 0
+    for k in ("A", "wq", "sq", "ids", "off", "C"):
+        assert moe(**{k: z}) == 1, k
+    # misaligned pointers
+    assert moe(A=ctypes.c_void_p(8)) == 2
+    assert moe(ids=ctypes.c_void_p(18)) == 2
+    assert moe(tw=ctypes.c_void_p(2)) == 2
+    # more row blocks than one grid column holds
+    assert moe(P=1 << 24, E=4096, out_rows=1 << 24) == 2
+    # A bytes beyond the 32-bit buffer range
+    assert moe(a_rows=1 << 20, K=1024) == 2
+
+
 def test_python_binding_validation():
     codes, scales = _rand_weights(4, 64, 0, 1)
     with pytest.raises(ValueError):

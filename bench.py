@@ -25,6 +25,10 @@ Printed as the last stdout line, one JSON object:
                PFLOP/s dense BF16 matrix-core peak
   fp16         the same decode step and prefill with FP16 activations and
                output (fp4_gemm_f16; FP16 matrix-core peak 2.5 PFLOP/s)
+  moe          the grouped MoE GEMM (fp4_moe_gemm): 128 experts, top-4,
+               fused gate/up N = 5760, K = 2880, MXFP4, 16 and 256 tokens;
+               algorithmic bytes = the routed-to experts' packed weights +
+               gathered activations + outputs
   cpu_baseline the CPU oracle (float64 NumPy) timed on a bounded sample
 """
 
@@ -76,6 +80,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true", help="skip the FP16-activation decode and prefill lines")
+    ap.add_argument("--no-moe", action="store_true", help="skip the grouped MoE GEMM lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (known bytes for HBM counter scaling)")
     return ap.parse_args()
@@ -190,6 +195,57 @@ def fp16_lines(args, F, torch, layers, A_bf16, WS, dev, m):
             tot_f += 2.0 * mp * l.N * l.K
         out["prefill_TFLOP/s"] = round(tot_f / tot_t / 1e6, 1)
         out["prefill_frac_mfma"] = round(tot_f / tot_t / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)
+    return out
+
+
+def moe_lines(args, F, torch, synth, dev):
+    """Grouped MoE GEMM at 16 and 256 tokens.  The expert weights are random
+    packed bytes made on the device (the packed layout is a permutation of
+    the codes, so random bytes are random codes; E8M0 scale bytes 121 ..
+    129): the timing does not depend on the values, and the parity of these
+    shapes is covered by the GPU tests with seeded codes.  Two copies of all
+    experts (2 x 1.13 GB) alternate between launches so the 256 MB
+    last-level cache cannot serve the weights."""
+    E, topk, N, K, fmt = 128, 4, 5760, 2880, 1
+    nw, ns = F.repack_size(N, K, fmt)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    copies = []
+    for _ in range(2):
+        wq = torch.randint(0, 256, (E * nw,), dtype=torch.uint8, device=dev, generator=gen)
+        sq = torch.randint(121, 130, (E * ns,), dtype=torch.uint8, device=dev, generator=gen)
+        copies.append((wq, sq))
+    lib = F.lib()
+    stream = F._c_vp(torch.cuda.current_stream().cuda_stream)
+    out = {"experts": E, "topk": topk, "N": N, "K": K, "weights": "mxfp4", "activations": "bf16"}
+    for T in (16, 256):
+        ids, offs, topw = synth.moe_routing(T, topk, E, seed=4242 + T)
+        a = torch.randn((T, K), device=dev).to(torch.bfloat16)
+        c = torch.empty((T * topk, N), dtype=torch.bfloat16, device=dev)
+        ids_d, offs_d, topw_d = (torch.from_numpy(ids).to(dev), torch.from_numpy(offs).to(dev),
+                                 torch.from_numpy(topw).to(dev))
+        calls = []
+        for wq, sq in copies:
+            argv = (F._dev_ptr(a), F._dev_ptr(wq), F._dev_ptr(sq), F._dev_ptr(ids_d), F._dev_ptr(offs_d),
+                    F._dev_ptr(topw_d), F._dev_ptr(c), T, topk, T * topk, ids.size, E, N, K, fmt, stream)
+            calls.append(argv)
+
+        def call(s, calls=calls):
+            st = lib.fp4_moe_gemm(*calls[s % 2])
+            if st:
+                F._check(st, "fp4_moe_gemm")
+        for s in range(5):
+            call(s)
+        torch.cuda.synchronize()
+        us = timed(call, args.prefill_launches)
+        active = int(np.count_nonzero(np.diff(offs)))
+        b = active * (N * K // 2 + N * K // 32) + ids.size * K * 2 + ids.size * N * 2
+        fl = 2.0 * ids.size * N * K
+        out[f"T{T}"] = {"us": round(us, 2), "active_experts": active, "assignments": int(ids.size),
+                        "GB/s": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "TFLOP/s": round(fl / us / 1e6, 2)}
+    del copies
+    torch.cuda.empty_cache()
     return out
 
 
@@ -314,6 +370,12 @@ def main():
         log(f"fp16: decode step {fp16['decode_step_us']} us -> {fp16['decode_GB/s']} GB/s; "
             f"prefill m=256 {fp16['prefill_TFLOP/s']} TFLOP/s")
 
+    moe = None
+    if not args.no_moe:
+        moe = moe_lines(args, F, torch, synth, dev)
+        log("moe: " + ", ".join(f"T={t}: {moe[f'T{t}']['us']} us, {moe[f'T{t}']['GB/s']} GB/s"
+                                for t in (16, 256)))
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(probs)
 
     out = {
@@ -341,6 +403,7 @@ def main():
         "layers": per_layer,
         "prefill": prefill,
         "fp16": fp16,
+        "moe": moe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

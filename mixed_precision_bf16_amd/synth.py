@@ -214,18 +214,7 @@ class MoeProblem:
         return self.a_bits.shape[0]
 
 
-def make_moe(T: int, topk: int, E: int, N: int, K: int, fmt: int, seed: int, *, per_assignment_a: bool = False,
-             with_weights: bool = True, skew: float = 0.0) -> MoeProblem:
-    """Seeded synthetic MoE routing and weights.  Each token picks topk
-    distinct experts, uniformly (skew = 0) or with probability proportional
-    to (rank + 1)^-skew over a random expert order (skew > 0 makes a few
-    experts hold many rows and leaves others empty); assignment id =
-    token * topk + slot.  Routing weights are uniform in [0, 1) rounded to
-    FP32.  A holds one row per token (a_div = topk) or, with
-    per_assignment_a, one row per assignment (a_div = 1).  Codes, scales and
-    activations follow the dense generators' distributions.  Draw order:
-    routing -> weights -> codes -> scales -> A."""
-    rng = np.random.Generator(np.random.PCG64(seed))
+def _moe_routing(rng, T, topk, E, with_weights, skew):
     if skew > 0:
         p = (np.arange(E) + 1.0) ** -skew
         p = p[np.argsort(rng.permutation(E))] / p.sum()
@@ -239,6 +228,29 @@ def make_moe(T: int, topk: int, E: int, N: int, K: int, fmt: int, seed: int, *, 
     sorted_ids = ids[order].astype(np.int32)
     counts = np.bincount(expert_of, minlength=E)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return sorted_ids, offsets, topw
+
+
+def moe_routing(T: int, topk: int, E: int, seed: int, *, with_weights: bool = True, skew: float = 0.0):
+    """The routing part of make_moe alone (same seed, same draws): returns
+    (sorted_ids, offsets, topw)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _moe_routing(rng, T, topk, E, with_weights, skew)
+
+
+def make_moe(T: int, topk: int, E: int, N: int, K: int, fmt: int, seed: int, *, per_assignment_a: bool = False,
+             with_weights: bool = True, skew: float = 0.0) -> MoeProblem:
+    """Seeded synthetic MoE routing and weights.  Each token picks topk
+    distinct experts, uniformly (skew = 0) or with probability proportional
+    to (rank + 1)^-skew over a random expert order (skew > 0 makes a few
+    experts hold many rows and leaves others empty); assignment id =
+    token * topk + slot.  Routing weights are uniform in [0, 1) rounded to
+    FP32.  A holds one row per token (a_div = topk) or, with
+    per_assignment_a, one row per assignment (a_div = 1).  Codes, scales and
+    activations follow the dense generators' distributions.  Draw order:
+    routing -> weights -> codes -> scales -> A."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    sorted_ids, offsets, topw = _moe_routing(rng, T, topk, E, with_weights, skew)
     codes = np.stack([_draw_codes(rng, N, K) for _ in range(E)])
     scales = np.stack([_draw_scales(rng, N, K, fmt) for _ in range(E)])
     a_rows = T * topk if per_assignment_a else T

@@ -152,6 +152,41 @@ int fp4_dequant(const void* wq, const void* sq, void* W_bf16, int64_t N, int64_t
 int fp4_dequant_f16(const void* wq, const void* sq, void* W_f16, int64_t N, int64_t K, int format,
                     void* stream);
 
+/* fp4_gemm / fp4_gemm_f16 with a per-tensor output scale:
+ *     C = alpha * (A . dequant(W)^T)
+ * act_type 0: BF16 A and C (as fp4_gemm), 1: FP16 (as fp4_gemm_f16).  alpha
+ * is the second-level FP32 scale of a two-level NVFP4 checkpoint (not on the
+ * pages; the offline quantizer below takes the same alpha), applied to the
+ * FP32 accumulator before rounding.  alpha must be finite with |alpha| in
+ * [2^-100, 2^100], else FP4_ERR_VALUE; alpha = 1 gives bit-identical results
+ * to fp4_gemm / fp4_gemm_f16.  act_type outside {0, 1} is FP4_ERR_FORMAT.
+ * Everything else (workspace, alignment, errors, determinism) as fp4_gemm. */
+int fp4_gemm_ex(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
+                int format, int act_type, float alpha, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Offline quantizer on the device: BF16 weights -> FP4 codes and block scales
+ * in the source order fp4_repack takes (mhpq.cn FP4 GEMM article: block
+ * scaling with the block maximum, section 2.2; nearest grid point, section
+ * 2.1; no zero scale for an all-zero block, section 5.2).
+ *   W       device, BF16 [N][K] row-major, 16-byte aligned
+ *   codes   device, uint8 [N][K/2] (element 2j in the low nibble), aligned
+ *           to G/2 bytes
+ *   scales  device, uint8 [N][K/G]
+ * Per block of G elements, in IEEE FP32 (correctly rounded operations):
+ *   NVFP4: scale = E4M3 round-to-nearest-even of (amax / 6) / alpha,
+ *          saturated at 448 and at least 2^-9 (never zero);
+ *   MXFP4: scale byte = clamp(floor(log2(amax / alpha)) - 2 + 127, 0, 254)
+ *          (the OCP MX rule); byte 0 makes every code of the block 0;
+ *   code = nearest E2M1 value to |x| / (alpha * scale), ties to the even
+ *   mantissa bit, saturating at +-6; no negative zero; NaN -> 0, +-Inf ->
+ *   +-6 with the largest scale.
+ * alpha > 0, finite, in [2^-100, 2^100] (else FP4_ERR_VALUE); quantizing with
+ * alpha and multiplying by it with fp4_gemm_ex reproduces the tensor's scale.
+ * N, K in 1 .. 2^24 with K % G == 0 (else FP4_ERR_SHAPE).  Asynchronous on
+ * `stream`. */
+int fp4_quantize(const void* W, void* codes, void* scales, int64_t N, int64_t K, int format, float alpha,
+                 void* stream);
+
 /* Grouped mixture-of-experts GEMM with BF16 activations (the petit-kernel
  * page, "Features": fused MoE kernels for BF16 and MXFP4 workloads; both FP4
  * formats are accepted).  For expert e = 0 .. E-1 and every assignment id

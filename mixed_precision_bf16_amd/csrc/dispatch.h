@@ -51,13 +51,13 @@ struct MoeArgs {
 // Launch one GEMM kernel on stream s (P: FP32 partials of a K split, else
 // null).  False when the shape is not compiled.
 bool launch_decode_bf16(int fmt, int MB, const DecodeShape& d, const void* A, const void* wq, const void* sq,
-                        void* C, float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s);
+                        void* C, float* P, int M, int N, int K, int KB, int SB, int NT, float alpha, hipStream_t s);
 bool launch_decode_f16(int fmt, int MB, const DecodeShape& d, const void* A, const void* wq, const void* sq, void* C,
-                       float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s);
+                       float* P, int M, int N, int K, int KB, int SB, int NT, float alpha, hipStream_t s);
 bool launch_prefill_bf16(int fmt, const PrefillShape& t, const void* A, const void* wq, const void* sq, void* C,
-                         float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s);
+                         float* P, int M, int N, int K, int KB, int SB, int NT, float alpha, hipStream_t s);
 bool launch_prefill_f16(int fmt, const PrefillShape& t, const void* A, const void* wq, const void* sq, void* C,
-                        float* P, int M, int N, int K, int KB, int SB, int NT, hipStream_t s);
+                        float* P, int M, int N, int K, int KB, int SB, int NT, float alpha, hipStream_t s);
 
 // Compiled MoE shapes (BF16 activations): X(MB, TN, NWN); one K group, no K
 // split.  `items` bounds the number of row blocks (grid height).

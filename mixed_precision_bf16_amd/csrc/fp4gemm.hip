@@ -1,6 +1,8 @@
 // C ABI of the FP4 GEMM (include/fp4gemm.h): argument checks, shape choice and
 // launches.  The kernels are in kernels.h; the decode and prefill kernels are
 // instantiated in their own translation units (dispatch.h).
+#include <math.h>
+
 #include <algorithm>
 #include <atomic>
 
@@ -134,13 +136,13 @@ static bool decode_compiled(int MB, const DecodeShape& d) {
     return false;
 }
 
-static void launch_reduce(int act, const float* P, void* C, int64_t total, int S, hipStream_t s) {
+static void launch_reduce(int act, const float* P, void* C, int64_t total, int S, float alpha, hipStream_t s) {
     const int64_t threads = (total + 3) / 4;
     const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
     if (act == 0)
-        reduce_partials<0><<<grid, block, 0, s>>>(P, (uint16_t*)C, total, S);
+        reduce_partials<0><<<grid, block, 0, s>>>(P, (uint16_t*)C, total, S, alpha);
     else
-        reduce_partials<1><<<grid, block, 0, s>>>(P, (uint16_t*)C, total, S);
+        reduce_partials<1><<<grid, block, 0, s>>>(P, (uint16_t*)C, total, S, alpha);
 }
 
 static PrefillShape prefill_override() {
@@ -182,23 +184,23 @@ static PrefillShape pick_prefill(int fmt, int64_t M, int64_t N, int NT, int SB) 
 }
 
 static int launch_gemm(int fmt, int act, const void* A, const void* wq, const void* sq, void* C, void* ws, int M,
-                       int N, int K, int KB, int SB, int NT, hipStream_t s) {
+                       int N, int K, int KB, int SB, int NT, float alpha, hipStream_t s) {
     if (M <= 64) {
         const int MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
         const DecodeShape d = pick_decode(fmt, MB, M, N, NT, SB);
         float* P = d.s > 1 ? static_cast<float*>(ws) : nullptr;
-        const bool ok = act == 0 ? launch_decode_bf16(fmt, MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, s)
-                                 : launch_decode_f16(fmt, MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, s);
+        const bool ok = act == 0 ? launch_decode_bf16(fmt, MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, s)
+                                 : launch_decode_f16(fmt, MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, s);
         if (!ok) return FP4_ERR_SHAPE;
-        if (P) launch_reduce(act, P, C, (int64_t)M * N, d.s, s);
+        if (P) launch_reduce(act, P, C, (int64_t)M * N, d.s, alpha, s);
         return FP4_OK;
     }
     const PrefillShape t = pick_prefill(fmt, M, N, NT, SB);
     float* P = t.s > 1 ? static_cast<float*>(ws) : nullptr;
-    const bool ok = act == 0 ? launch_prefill_bf16(fmt, t, A, wq, sq, C, P, M, N, K, KB, SB, NT, s)
-                             : launch_prefill_f16(fmt, t, A, wq, sq, C, P, M, N, K, KB, SB, NT, s);
+    const bool ok = act == 0 ? launch_prefill_bf16(fmt, t, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, s)
+                             : launch_prefill_f16(fmt, t, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, s);
     if (!ok) return FP4_ERR_SHAPE;
-    if (P) launch_reduce(act, P, C, (int64_t)M * N, t.s, s);
+    if (P) launch_reduce(act, P, C, (int64_t)M * N, t.s, alpha, s);
     return FP4_OK;
 }
 
@@ -214,10 +216,18 @@ static size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
     return decode_workspace_bytes(pick_decode(fmt, MB, M, N, NT, SB), M, N);
 }
 
+// alpha: finite, |alpha| in [2^-100, 2^100] or exactly 1 (checked by the entries).
+static bool alpha_ok(float alpha) {
+    const float a = fabsf(alpha);
+    return a == 1.0f || (a >= 0x1p-100f && a <= 0x1p100f);
+}
+
 static int gemm_impl(int act, const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N,
-                     int64_t K, int format, void* workspace, size_t workspace_bytes, void* stream) {
+                     int64_t K, int format, float alpha, void* workspace, size_t workspace_bytes, void* stream) {
     int st = fp4_check_weight_shape(N, K, format);
     if (st != FP4_OK) return st;
+    if (act != 0 && act != 1) return FP4_ERR_FORMAT;
+    if (!alpha_ok(alpha)) return FP4_ERR_VALUE;
     if (m < 0 || m > (int64_t(1) << 20)) return FP4_ERR_SHAPE;
     if (m == 0) return FP4_OK;
     if (!A || !wq || !sq || !C) return FP4_ERR_NULL;
@@ -233,7 +243,7 @@ static int gemm_impl(int act, const void* A, const void* wq, const void* sq, voi
     const int64_t Np = padded_n(N), Kp = padded_k(K);
     const int KB = int(Kp / kChunkK), SB = int(Kp / kScaleBlockK), NT = int(Np / kTileN);
     (void)hipGetLastError();
-    st = launch_gemm(format, act, A, wq, sq, C, workspace, int(m), int(N), int(K), KB, SB, NT,
+    st = launch_gemm(format, act, A, wq, sq, C, workspace, int(m), int(N), int(K), KB, SB, NT, alpha,
                      reinterpret_cast<hipStream_t>(stream));
     if (st != FP4_OK) return st;
     return launch_status();
@@ -315,9 +325,44 @@ static int moe_impl(const void* A, const void* wq, const void* sq, const int32_t
     return launch_status();
 }
 
+static int quantize_impl(const void* W, void* codes, void* scales, int64_t N, int64_t K, int format, float alpha,
+                         void* stream) {
+    if (format != FP4_NVFP4 && format != FP4_MXFP4) return FP4_ERR_FORMAT;
+    const int64_t G = format == FP4_NVFP4 ? 16 : 32;
+    if (N < 1 || K < G || K % G || N > (int64_t(1) << 24) || K > (int64_t(1) << 24)) return FP4_ERR_SHAPE;
+    if (!W || !codes || !scales) return FP4_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(W) & 15) || (reinterpret_cast<uintptr_t>(codes) & (G / 2 - 1)))
+        return FP4_ERR_SHAPE;
+    if (!(alpha > 0.0f) || !alpha_ok(alpha)) return FP4_ERR_VALUE;
+    int st = check_device();
+    if (st != FP4_OK) return st;
+    const int64_t groups = N * (K / G);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const dim3 grid((unsigned)((groups + 255) / 256)), block(256);
+    if (format == FP4_NVFP4)
+        quantize_kernel<0><<<grid, block, 0, s>>>((const uint16_t*)W, (uint8_t*)codes, (uint8_t*)scales, groups,
+                                                  alpha);
+    else
+        quantize_kernel<1><<<grid, block, 0, s>>>((const uint16_t*)W, (uint8_t*)codes, (uint8_t*)scales, groups,
+                                                  alpha);
+    return launch_status();
+}
+
 }  // namespace fp4
 
 using namespace fp4;
+
+extern "C" int fp4_gemm_ex(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
+                           int format, int act_type, float alpha, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    return gemm_impl(act_type, A, wq, sq, C, m, N, K, format, alpha, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fp4_quantize(const void* W, void* codes, void* scales, int64_t N, int64_t K, int format, float alpha,
+                            void* stream) {
+    return quantize_impl(W, codes, scales, N, K, format, alpha, stream);
+}
 
 extern "C" int fp4_moe_gemm(const void* A, const void* wq, const void* sq, const int32_t* sorted_ids,
                             const int32_t* expert_offsets, const float* topk_weights, void* C, int64_t a_rows,
@@ -338,12 +383,12 @@ extern "C" int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int form
 
 extern "C" int fp4_gemm(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
                         int format, void* workspace, size_t workspace_bytes, void* stream) {
-    return gemm_impl(0, A, wq, sq, C, m, N, K, format, workspace, workspace_bytes, stream);
+    return gemm_impl(0, A, wq, sq, C, m, N, K, format, 1.0f, workspace, workspace_bytes, stream);
 }
 
 extern "C" int fp4_gemm_f16(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
                             int format, void* workspace, size_t workspace_bytes, void* stream) {
-    return gemm_impl(1, A, wq, sq, C, m, N, K, format, workspace, workspace_bytes, stream);
+    return gemm_impl(1, A, wq, sq, C, m, N, K, format, 1.0f, workspace, workspace_bytes, stream);
 }
 
 extern "C" int fp4_dequant(const void* wq, const void* sq, void* W_bf16, int64_t N, int64_t K, int format,

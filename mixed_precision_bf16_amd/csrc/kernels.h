@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
                                                              const uint8_t* __restrict__ sq,
                                                              uint16_t* __restrict__ C, float* __restrict__ P, int M,
                                                              int N, int K, int KB, int SB, int NT, int S,
-                                                             MoeArgs moe = MoeArgs{}) {
+                                                             float alpha, MoeArgs moe = MoeArgs{}) {
     typedef u32x4 SW;
     constexpr int kRows = 16 * MB;  // activation rows; one 1 KiB load per row per block
     // Activation load instructions per wave per block.  When NWN does not
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
             if (m >= M) continue;
             const int id = moe.ids[row0 + m];
             if (id < 0 || id >= moe.out_rows) continue;
-            const float w = moe.topw ? moe.topw[id] : 1.0f;
+            const float w = (moe.topw ? moe.topw[id] : 1.0f) * alpha;
 #pragma unroll
             for (int tt = 0; tt < TN; ++tt) store_frag<ACT>(C, acc[tt][mb] * w, id, (tile0 + tt) * kTileN + 4 * j,
                                                             moe.out_rows, N);
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
         for (int mb = 0; mb < MB; ++mb) {
             const int m = mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
             if (P == nullptr) {
-                store_frag<ACT>(C, acc[tt][mb], m, n0, M, N);
+                store_frag<ACT>(C, acc[tt][mb] * alpha, m, n0, M, N);
             } else if (m < M) {
                 float* dst = P + ((size_t)ks * M + m) * N + n0;
                 if ((N & 3) == 0 && n0 + 3 < N) {
@@ -512,23 +512,25 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
         }
 }
 
-// Y = sum over s of the S partial products P[s][M][N] (in order s = 0, 1, ...),
-// rounded to BF16.  Four consecutive elements of the flattened [M][N] array
-// per thread.
+// Y = alpha x the sum over s of the S partial products P[s][M][N] (in order
+// s = 0, 1, ...), rounded to the output type.  Four consecutive elements of
+// the flattened [M][N] array per thread.
 template <int ACT>
 __global__ __launch_bounds__(256) void reduce_partials(const float* __restrict__ P, uint16_t* __restrict__ C,
-                                                       int64_t total, int S) {
+                                                       int64_t total, int S, float alpha) {
     const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (e >= total) return;
     if (e + 3 < total) {
         f32x4 v = *reinterpret_cast<const f32x4*>(P + e);
         for (int s = 1; s < S; ++s) v += *reinterpret_cast<const f32x4*>(P + (size_t)s * total + e);
+        v *= alpha;
         u32x2 o = {pack_out<ACT>(v.x, v.y), pack_out<ACT>(v.z, v.w)};
         *reinterpret_cast<u32x2*>(C + e) = o;
     } else {
         for (int64_t x = e; x < total; ++x) {
             float v = P[x];
             for (int s = 1; s < S; ++s) v += P[(size_t)s * total + x];
+            v *= alpha;
             C[x] = (uint16_t)(pack_out<ACT>(v, 0.f) & 0xFFFF);
         }
     }
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
                                                             const u32x4* __restrict__ wq,
                                                             const uint8_t* __restrict__ sq, uint16_t* __restrict__ C,
                                                             float* __restrict__ P, int M, int N, int K, int KB,
-                                                            int SB, int NT, int S) {
+                                                            int SB, int NT, int S, float alpha) {
     static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
     typedef u32x4 SW;
     constexpr int kThreads = 64 * WM * WN;
@@ -786,7 +788,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
         for (int mb = 0; mb < MBW; ++mb) {
             const int m = m0 + wm * MBW * 16 + mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
             if (P == nullptr) {
-                store_frag<ACT>(C, acc[tt][mb], m, n0, M, N);
+                store_frag<ACT>(C, acc[tt][mb] * alpha, m, n0, M, N);
             } else if (m < M) {
                 float* dst = P + ((size_t)ks * M + m) * N + n0;
                 if ((N & 3) == 0 && n0 + 3 < N) {
@@ -797,6 +799,100 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
                 }
             }
         }
+}
+
+// ------------------------------------------------------------ quantizer
+// Offline quantizer: BF16 weights -> E2M1 codes (two per byte, element 2j in
+// the low nibble) and one scale byte per G-element block, in the source
+// order fp4_repack takes.  Block scaling with the block's largest magnitude
+// and nearest-grid rounding (mhpq.cn FP4 GEMM article, sections 2.1, 2.2); an
+// all-zero block never gets a zero NVFP4 scale (section 5.2).  Every decision
+// is taken in IEEE FP32 with correctly rounded operations:
+//   NVFP4: scale byte = E4M3 round-to-nearest-even of (amax / 6) / alpha,
+//          saturated at 448, at least 2^-9 (byte 1);
+//   MXFP4: scale byte = clamp(floor(log2(amax / alpha)) - 2 + 127, 0, 254),
+//          255 never; byte 0 marks a zero block (all codes 0);
+//   S = alpha * scale, q = |x| / S, code = nearest E2M1 value to q with
+//   ties to the even mantissa bit, saturating at 6; the sign bit only on
+//   non-zero codes.  NaN elements give 0 (amax ignores them); infinities
+//   give +-6 and the largest scale.
+// One thread per block of G elements: the blocks of a row are consecutive
+// in memory, so a wave reads and writes contiguous bytes.
+
+// E4M3 byte of the nearest value to t >= 0 (ties to the even mantissa),
+// saturating at 448 (byte 0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+    if (!(t < 448.0f)) return 0x7Eu;
+    const uint32_t b = __float_as_uint(t);
+    const int e = int((b >> 23) & 0xFF) - 127;
+    if (e >= -6) {  // E4M3 normal range: keep 3 mantissa bits, round to nearest even
+        const uint32_t m3 = (b >> 20) & 7u, rem = b & 0xFFFFFu;
+        const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ? 1u : 0u;
+        return ((uint32_t)(e + 7) << 3) + m3 + up;  // a mantissa carry moves into the exponent
+    }
+    // subnormal range: value = f x 2^-9, f = round-half-even(t x 2^9) in 0 .. 8
+    // (f = 8 is 2^-6, whose byte 0x08 is the same integer)
+    return (uint32_t)rintf(t * 512.0f);
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t byte) {
+    const uint32_t e = byte >> 3, m = byte & 7u;
+    return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ W, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales, int64_t groups, float alpha) {
+    constexpr int G = FMT == 0 ? 16 : 32;
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= groups) return;
+    u32x4 v[G / 8];
+    const u32x4* src = reinterpret_cast<const u32x4*>(W + g * G);
+#pragma unroll
+    for (int i = 0; i < G / 8; ++i) v[i] = src[i];
+    float x[G];
+#pragma unroll
+    for (int i = 0; i < G / 2; ++i) {
+        const uint32_t d = v[i / 4][i % 4];
+        x[2 * i] = __uint_as_float(d << 16);
+        x[2 * i + 1] = __uint_as_float(d & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) amax = fmaxf(amax, fabsf(x[i]));  // fmaxf drops NaN operands
+    uint32_t sb;
+    float sval;
+    bool zero_block = false;
+    if constexpr (FMT == 0) {
+        sb = e4m3_rne(__fdiv_rn(__fdiv_rn(amax, 6.0f), alpha));
+        sb = sb == 0 ? 1u : sb;
+        sval = e4m3_decode(sb);
+    } else {
+        const float t = __fdiv_rn(amax, alpha);
+        const int ef = int((__float_as_uint(t) >> 23) & 0xFF);  // 0: zero or below 2^-126; 255: infinite
+        sb = ef == 255 ? 254u : (uint32_t)max(ef - 2, 0);
+        zero_block = sb == 0;
+        sval = __uint_as_float(sb << 23);  // 2^(sb - 127) for sb >= 1
+    }
+    const float S = __fmul_rn(alpha, sval);
+    uint32_t out[G / 8];
+#pragma unroll
+    for (int w = 0; w < G / 8; ++w) out[w] = 0;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const float q = __fdiv_rn(fabsf(x[i]), S);
+        uint32_t c = (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) +
+                     (uint32_t)(q >= 1.75f) + (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) + (uint32_t)(q > 5.0f);
+        if (zero_block) c = 0;
+        if (c != 0 && x[i] < 0.0f) c |= 8u;
+        out[i / 8] |= c << (4 * (i % 8));
+    }
+    if constexpr (FMT == 0) {
+        *reinterpret_cast<u32x2*>(codes + g * (G / 2)) = u32x2{out[0], out[1]};
+    } else {
+        *reinterpret_cast<u32x4*>(codes + g * (G / 2)) = u32x4{out[0], out[1], out[2], out[3]};
+    }
+    scales[g] = (uint8_t)sb;
 }
 
 // ------------------------------------------------------------ debug dequant

@@ -37,6 +37,9 @@ _SIGNATURES = {
                                     _c_sz, _c_vp]),
     "fp4_dequant": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
     "fp4_dequant_f16": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
+    "fp4_gemm_ex": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_float, _c_vp, _c_sz, _c_vp]),
+    "fp4_quantize": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, ctypes.c_float, _c_vp]),
     "fp4_moe_gemm": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                     _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
 }
@@ -149,10 +152,10 @@ def new_workspace(m: int, N: int, K: int, fmt: int, device="cuda"):
     return torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes else None
 
 
-def gemm(A, wq, sq, N: int, K: int, fmt: int, out=None, workspace=None, stream=None):
-    """Y = A . dequant(W)^T.  A: bfloat16 (fp4_gemm) or float16 (fp4_gemm_f16)
-    CUDA [m][K]; wq, sq: uint8 CUDA (packed).  Returns (or fills) a tensor
-    [m][N] of A's dtype."""
+def gemm(A, wq, sq, N: int, K: int, fmt: int, out=None, workspace=None, stream=None, alpha: float = 1.0):
+    """Y = alpha * A . dequant(W)^T.  A: bfloat16 (fp4_gemm) or float16
+    (fp4_gemm_f16) CUDA [m][K]; wq, sq: uint8 CUDA (packed).  alpha != 1 goes
+    through fp4_gemm_ex.  Returns (or fills) a tensor [m][N] of A's dtype."""
     import torch
     if A.dtype not in (torch.bfloat16, torch.float16) or A.dim() != 2 or not A.is_cuda or not A.is_contiguous():
         raise ValueError("A must be a contiguous 2-D bfloat16 or float16 CUDA tensor")
@@ -173,10 +176,30 @@ def gemm(A, wq, sq, N: int, K: int, fmt: int, out=None, workspace=None, stream=N
     if wsb and workspace is None:
         workspace = torch.zeros(wsb, dtype=torch.uint8, device=A.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if alpha != 1.0:
+        act = 0 if A.dtype == torch.bfloat16 else 1
+        _check(lib().fp4_gemm_ex(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), m, N, K, fmt, act, alpha,
+                                 _dev_ptr(workspace), ws_bytes, _stream_handle(stream)), "fp4_gemm_ex")
+        return out
     fn = lib().fp4_gemm if A.dtype == torch.bfloat16 else lib().fp4_gemm_f16
     _check(fn(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), m, N, K, fmt, _dev_ptr(workspace), ws_bytes,
               _stream_handle(stream)), "fp4_gemm")
     return out
+
+
+def quantize(W, fmt: int, alpha: float = 1.0, stream=None):
+    """fp4_quantize: BF16 CUDA weights [N][K] -> (codes uint8 [N][K/2], scales
+    uint8 [N][K/G]) on the device, in the source order repack() takes."""
+    import torch
+    if W.dtype != torch.bfloat16 or W.dim() != 2 or not W.is_cuda or not W.is_contiguous():
+        raise ValueError("W must be a contiguous 2-D bfloat16 CUDA tensor")
+    N, K = W.shape
+    G = 16 if fmt == NVFP4 else 32
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((N, max(K // G, 1)), dtype=torch.uint8, device=W.device)
+    _check(lib().fp4_quantize(_dev_ptr(W), _dev_ptr(codes), _dev_ptr(scales), N, K, fmt, alpha,
+                              _stream_handle(stream)), "fp4_quantize")
+    return codes, scales
 
 
 def dequant(wq, sq, N: int, K: int, fmt: int, out=None, stream=None, dtype=None):

@@ -205,6 +205,27 @@ def test_moe_argument_errors_before_any_hip_call():
     assert moe(a_rows=1 << 20, K=1024) == 2
 
 
+def test_gemm_ex_and_quantize_argument_errors_before_any_hip_call():
+    lib = F.lib()
+    d = ctypes.c_void_p(16)
+    z = ctypes.c_void_p(0)
+    ex = lib.fp4_gemm_ex
+    assert ex(d, d, d, d, 16, 64, 64, 0, 2, 1.0, None, 0, None) == 3          # act_type
+    for bad in (float("nan"), float("inf"), 0.0, 2.0 ** -101, 2.0 ** 101):
+        assert ex(d, d, d, d, 16, 64, 64, 0, 0, bad, None, 0, None) == 4, bad
+    assert ex(z, d, d, d, 16, 64, 64, 0, 0, 0.5, None, 0, None) == 1
+    assert ex(z, z, z, z, 0, 64, 64, 0, 1, 0.5, None, 0, None) == 0           # m = 0 no-op
+    q = lib.fp4_quantize
+    assert q(d, d, d, 4, 64, 9, 1.0, None) == 3
+    assert q(d, d, d, 4, 24, 0, 1.0, None) == 2 and q(d, d, d, 4, 48, 1, 1.0, None) == 2
+    assert q(d, d, d, 0, 64, 0, 1.0, None) == 2
+    assert q(z, d, d, 4, 64, 0, 1.0, None) == 1 and q(d, d, z, 4, 64, 0, 1.0, None) == 1
+    assert q(ctypes.c_void_p(8), d, d, 4, 64, 0, 1.0, None) == 2
+    assert q(d, ctypes.c_void_p(20), d, 4, 64, 1, 1.0, None) == 2              # MXFP4 codes: 16-byte stores
+    for bad in (float("nan"), -1.0, 0.0, float("inf")):
+        assert q(d, d, d, 4, 64, 0, bad, None) == 4, bad
+
+
 def test_python_binding_validation():
     codes, scales = _rand_weights(4, 64, 0, 1)
     with pytest.raises(ValueError):

@@ -1,0 +1,131 @@
+"""GPU parity of the offline quantizer (fp4_quantize) and of the per-tensor
+output scale (fp4_gemm_ex), through the C ABI, against the CPU oracle.
+
+Bars: quantizer codes and scale bytes bit-exact against
+oracle.quantize_reference (integer output decided in FP32 on both sides);
+fp4_gemm_ex with alpha = 2^-3 bit-identical to fp4_gemm's output scaled by
+2^-3, and any alpha within alpha x the GEMM tolerance of the oracle.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from mixed_precision_bf16_amd import fp4gemm as F
+from mixed_precision_bf16_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gfx950():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    if not name.startswith("gfx950"):
+        pytest.skip(f"needs gfx950, found {name}")
+    F.lib()
+    yield
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _weights(N, K, fmt, seed, specials=True):
+    """BF16 weight bits: N(0,1) times a per-row power of two in 2^-8 .. 2^8,
+    plus (specials) zero blocks, exact grid midpoints, NaN, +-Inf and
+    negative values that round to zero."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    G = 16 if fmt == 0 else 32
+    w = (rng.standard_normal((N, K)) * np.exp2(rng.integers(-8, 9, size=(N, 1)))).astype(np.float32)
+    if specials and N >= 4:
+        w[0, :G] = 0.0                                             # zero block
+        mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+        blk = np.zeros(G, np.float32)
+        blk[0] = 6.0                                               # block max 6 -> scale 1
+        blk[1:1 + 7] = mids
+        blk[8:15] = -mids
+        w[1, :G] = blk
+        if K >= 4 * G:
+            w[2, G:2 * G] = -1e-30
+            w[2, 2 * G] = -7.0
+            w[3, 3 * G] = np.nan
+            w[3, 3 * G + 1] = 2.0
+            w[3, 2 * G] = np.inf
+            w[3, 2 * G + 1] = -np.inf
+    bits = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return bits
+
+
+@pytest.mark.parametrize("fmt,N,K,alpha", [(0, 37, 512, 1.0), (1, 37, 512, 1.0), (0, 1000, 8192, 1.0),
+                                           (1, 640, 2880, 1.0), (0, 64, 1024, 0.37), (1, 64, 1024, 2.0 ** -7),
+                                           (0, 5, 16, 1.0), (1, 3, 32, 3.0)])
+def test_quantize_bit_exact(fmt, N, K, alpha):
+    bits = _weights(N, K, fmt, seed=N + K + fmt)
+    _say("quantize", fmt, N, K, alpha)
+    want_c, want_s = oracle.quantize_reference(bits, fmt, alpha)
+    W = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    c, s = F.quantize(W, fmt, alpha)
+    torch.cuda.synchronize()
+    c, s = c.cpu().numpy(), s.cpu().numpy()
+    assert np.array_equal(s, want_s), np.argwhere(s != want_s)[:5]
+    assert np.array_equal(c, want_c), np.argwhere(c != want_c)[:5]
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_quantize_then_gemm_parity(fmt):
+    """Device-quantized weights through repack and the GEMM: within the
+    tolerance of the oracle's GEMM on the same codes and scales, and
+    fp4_gemm_ex with the quantizer's alpha matches alpha x that."""
+    N, K, m, alpha = 520, 2048, 16, 0.5 if fmt == 0 else 1.0
+    bits = _weights(N, K, fmt, seed=11 + fmt, specials=False)
+    _say("quantize -> gemm", fmt)
+    W = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    c, s = F.quantize(W, fmt, alpha)
+    codes, scales = c.cpu().numpy(), s.cpu().numpy()
+    wq, sq = F.upload(*F.repack(codes, scales, N, K, fmt))
+    p = synth.make_random(m, N, K, fmt, seed=3)
+    A = torch.from_numpy(p.a_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    y = F.gemm(A, wq, sq, N, K, fmt, alpha=alpha)
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.gemm_reference(p.a_bits, codes, scales, K, fmt)
+    y_ref, bound = oracle.scaled_gemm_reference(y_ref, bound, alpha)
+    yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert oracle.check_tolerance(yb, y_ref, bound).all()
+    # the quantized weights approximate W: |alpha x dequant - w| <= alpha x scale wherever |w| <= 6 alpha
+    # x scale; elements beyond (the block maximum when the scale rounded down) saturate to 6 alpha x scale
+    w = oracle.bf16_bits_to_f64(bits)
+    d = alpha * oracle.dequant_weights(codes, scales, K, fmt)
+    G = 16 if fmt == 0 else 32
+    S = alpha * np.repeat(oracle.scale_value(scales, fmt), G, axis=1)
+    inside = np.abs(w) <= 6 * S
+    assert np.all((np.abs(d - w) <= S * (1 + 1e-6))[inside])
+    assert np.all((np.abs(d) == 6 * S)[~inside])
+
+
+@pytest.mark.parametrize("m,N,K,fmt,act", [(16, 8192, 8192, 0, 0), (16, 8192, 28672, 0, 0), (256, 1024, 4096, 0, 0),
+                                           (100, 520, 2048, 1, 0), (16, 4096, 8192, 0, 1), (256, 512, 2048, 1, 1),
+                                           (5, 40, 48, 0, 0)])
+def test_gemm_ex_alpha(m, N, K, fmt, act):
+    """alpha = 2^-3 is exact: bit-identical to the unscaled output times 2^-3
+    (decode with and without a K split, prefill, both activation types);
+    alpha = 0.3 within 0.3 x the tolerance of the oracle."""
+    tdt = torch.bfloat16 if act == 0 else torch.float16
+    p = synth.make_random(m, N, K, fmt, seed=m + N + K, act="bf16" if act == 0 else "f16")
+    _say("gemm_ex", m, N, K, fmt, act)
+    wq, sq = F.upload(*F.repack(p.codes, p.scales, N, K, fmt))
+    A = torch.from_numpy(p.a_bits.view(np.int16)).cuda().view(tdt)
+    y1 = F.gemm(A, wq, sq, N, K, fmt)
+    y8 = F.gemm(A, wq, sq, N, K, fmt, alpha=0.125)
+    y3 = F.gemm(A, wq, sq, N, K, fmt, alpha=0.3)
+    torch.cuda.synchronize()
+    assert torch.equal((y1.float() * 0.125).to(tdt), y8)
+    yb = y3.view(torch.int16).cpu().numpy().view(np.uint16)
+    rows = np.arange(N) if N <= 1024 else np.unique(np.concatenate([np.arange(32), np.arange(N - 32, N),
+                                                                    np.arange(0, N, 97)]))
+    y_ref, bound = oracle.gemm_reference(p.a_bits, p.codes[rows], p.scales[rows], K, fmt, p.act)
+    y_ref, bound = oracle.scaled_gemm_reference(y_ref, bound, 0.3)
+    assert oracle.check_tolerance(yb[:, rows], y_ref, bound, act=p.act).all()

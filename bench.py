@@ -25,6 +25,9 @@ Printed as the last stdout line, one JSON object:
                PFLOP/s dense BF16 matrix-core peak
   fp16         the same decode step and prefill with FP16 activations and
                output (fp4_gemm_f16; FP16 matrix-core peak 2.5 PFLOP/s)
+  quantize     the offline quantizer (fp4_quantize) on the gate/up weight
+               (57344 x 8192 BF16): GB/s of BF16 read + codes and scales
+               written, both formats
   moe          the grouped MoE GEMM (fp4_moe_gemm): 128 experts, top-4,
                fused gate/up N = 5760, K = 2880, MXFP4, 16 and 256 tokens;
                algorithmic bytes = the routed-to experts' packed weights +
@@ -81,6 +84,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true", help="skip the FP16-activation decode and prefill lines")
     ap.add_argument("--no-moe", action="store_true", help="skip the grouped MoE GEMM lines")
+    ap.add_argument("--no-quantize", action="store_true", help="skip the quantizer line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (known bytes for HBM counter scaling)")
     return ap.parse_args()
@@ -195,6 +199,39 @@ def fp16_lines(args, F, torch, layers, A_bf16, WS, dev, m):
             tot_f += 2.0 * mp * l.N * l.K
         out["prefill_TFLOP/s"] = round(tot_f / tot_t / 1e6, 1)
         out["prefill_frac_mfma"] = round(tot_f / tot_t / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)
+    return out
+
+
+def quantize_lines(args, F, torch, dev):
+    """fp4_quantize on a 57344 x 8192 BF16 weight drawn N(0, 1) on the device;
+    mean of back-to-back launches alternating two weight copies (2 x 940 MB,
+    beyond the last-level cache).  Algorithmic bytes: 2 per weight read, 1/2
+    per weight of codes and 1/G of scales written."""
+    N, K = 57344, 8192
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(99)
+    Ws = [torch.randn((N, K), device=dev, generator=gen).to(torch.bfloat16) for _ in range(2)]
+    lib = F.lib()
+    stream = F._c_vp(torch.cuda.current_stream().cuda_stream)
+    out = {"N": N, "K": K}
+    for fmt, G in ((0, 16), (1, 32)):
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((N, K // G), dtype=torch.uint8, device=dev)
+        argv = [(F._dev_ptr(W), F._dev_ptr(codes), F._dev_ptr(scales), N, K, fmt, 1.0, stream) for W in Ws]
+
+        def call(s, argv=argv):
+            st = lib.fp4_quantize(*argv[s % 2])
+            if st:
+                F._check(st, "fp4_quantize")
+        for s in range(3):
+            call(s)
+        torch.cuda.synchronize()
+        us = timed(call, args.prefill_launches)
+        b = N * K * 2 + N * K // 2 + N * K // G
+        out["nvfp4" if fmt == 0 else "mxfp4"] = {"us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
+                                                 "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del Ws
+    torch.cuda.empty_cache()
     return out
 
 
@@ -370,6 +407,12 @@ def main():
         log(f"fp16: decode step {fp16['decode_step_us']} us -> {fp16['decode_GB/s']} GB/s; "
             f"prefill m=256 {fp16['prefill_TFLOP/s']} TFLOP/s")
 
+    quant = None
+    if not args.no_quantize:
+        quant = quantize_lines(args, F, torch, dev)
+        log(f"quantize 57344x8192: nvfp4 {quant['nvfp4']['us']} us ({quant['nvfp4']['GB/s']} GB/s), "
+            f"mxfp4 {quant['mxfp4']['us']} us ({quant['mxfp4']['GB/s']} GB/s)")
+
     moe = None
     if not args.no_moe:
         moe = moe_lines(args, F, torch, synth, dev)
@@ -404,6 +447,7 @@ def main():
         "prefill": prefill,
         "fp16": fp16,
         "moe": moe,
+        "quantize": quant,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -878,11 +878,27 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     uint32_t out[G / 8];
 #pragma unroll
     for (int w = 0; w < G / 8; ++w) out[w] = 0;
+    // With alpha a power of two, S has at most 4 significant bits and x at
+    // most 8, so q = fl(|x| / S) lies on the same side of every midpoint c
+    // (at most 3 significant bits) as |x| does of c x S, which is exact in
+    // FP32: a quotient that is not c differs from it by at least 2^-8 / 300
+    // relative, far more than the half-ulp the division rounds by.  Then the
+    // decision needs no division (S below 2^120 keeps 5 S finite).
+    const bool exact_thresholds = (__float_as_uint(alpha) & 0x007FFFFFu) == 0u && S < 0x1p120f;
+    const float t0 = 0.25f * S, t1 = 0.75f * S, t2 = 1.25f * S, t3 = 1.75f * S, t4 = 2.5f * S, t5 = 3.5f * S,
+                t6 = 5.0f * S;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-        const float q = __fdiv_rn(fabsf(x[i]), S);
-        uint32_t c = (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) +
-                     (uint32_t)(q >= 1.75f) + (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) + (uint32_t)(q > 5.0f);
+        const float ax = fabsf(x[i]);
+        uint32_t c;
+        if (exact_thresholds) {
+            c = (uint32_t)(ax > t0) + (uint32_t)(ax >= t1) + (uint32_t)(ax > t2) + (uint32_t)(ax >= t3) +
+                (uint32_t)(ax > t4) + (uint32_t)(ax >= t5) + (uint32_t)(ax > t6);
+        } else {
+            const float q = __fdiv_rn(ax, S);
+            c = (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) + (uint32_t)(q >= 1.75f) +
+                (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) + (uint32_t)(q > 5.0f);
+        }
         if (zero_block) c = 0;
         if (c != 0 && x[i] < 0.0f) c |= 8u;
         out[i / 8] |= c << (4 * (i % 8));

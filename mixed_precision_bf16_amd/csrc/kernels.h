@@ -384,12 +384,17 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
         for (int u = 0; u < QB; ++u)
             if (alive[u]) *reinterpret_cast<u32x4*>(dst + ldst[u]) = ar[u];
     };
+    // Code blocks wholly past K (the zero padding of K to 512) are not
+    // fetched: an out-of-range offset makes the load return zeros without a
+    // memory access.
+    const int kb_valid = (K + kChunkK - 1) / kChunkK;
     auto w_issue = [&](auto slot_c, int chunk) {
         constexpr int SL = decltype(slot_c)::value;
         chunk = min(chunk, cmax);
+        const uint32_t voff = (uint32_t)lane * 16u + (chunk < kb_valid ? 0u : kOutOfRange);
 #pragma unroll
         for (int tt = 0; tt < TN; ++tt)
-            wr[SL][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, kLoadStream);
+            wr[SL][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], voff, chunk * 1024, kLoadStream);
     };
     auto lds_barrier = [] {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");

@@ -167,8 +167,9 @@ static bool prefill_compiled(const PrefillShape& t) {
 // waves (two per SIMD), each over all 128 rows of the block with two
 // n-tiles, so each dequantized fragment feeds 8 products and one wave's
 // vector work overlaps the other's matrix work (about 10 % faster than four
-// waves of four n-tiles); K is split until about 160 workgroups run (QKV 2,
-// O and down 4, gate_up 1).  FP4GEMM_PREFILL="WM,WN,MBW,TNW,S" overrides it.
+// waves of four n-tiles); the K split S minimizes the rounds of workgroups
+// per unit of work (QKV 3, O and down 4, gate_up 1 at m = 256).
+// FP4GEMM_PREFILL="WM,WN,MBW,TNW,S" overrides it.
 static PrefillShape pick_prefill(int fmt, int64_t M, int64_t N, int NT, int SB) {
     (void)fmt;
     (void)N;
@@ -178,8 +179,23 @@ static PrefillShape pick_prefill(int fmt, int64_t M, int64_t N, int NT, int SB) 
         return t;
     }
     t = PrefillShape{1, 8, 8, 2, 1};
+    // Time model fit to MI355X (m = 256): one workgroup per CU at a time
+    // (eight waves, 232 VGPRs); a round of workgroups over the whole K takes
+    // about 17 ns per K element, so a K split S runs ceil(blocks * S / 256)
+    // rounds of 1/S of that; a split also writes and reads S FP32 partials
+    // per output (about 5 TB/s) and pays the reduce launch (about 5 us).
     const int64_t blocks = ((M + 127) / 128) * ((NT + 15) / 16);
-    while (blocks * t.s < 160 && t.s < 8 && 2 * t.s <= SB) t.s *= 2;
+    const double t_round = 0.017e-6 * double(SB) * kScaleBlockK;
+    double best = 1e30;
+    for (int s = 1; s <= 8 && s <= SB; ++s) {
+        const double rounds = double((blocks * s + kCUs - 1) / kCUs);
+        const double split = s > 1 ? 5e-6 + double(s) * double(M) * double(N) * 8.0 / 5e12 : 0.0;
+        const double cost = rounds * t_round / s + split;
+        if (cost < best - 1e-9) {
+            best = cost;
+            t.s = s;
+        }
+    }
     return t;
 }
 

@@ -247,10 +247,11 @@ def test_workspace_size_is_a_split_k_partial_buffer():
             S, rem = divmod(b, 4 * m * N)
             assert rem == 0 and 2 <= S <= min(16, -(-K // 512)), (m, N, K, b)
     assert F.workspace_size(0, 8192, 8192, 0) == 0
-    # prefill m: split only while fewer than ~160 workgroups would run
-    for m, N, K in ((256, 8192, 8192), (256, 10240, 8192), (256, 8192, 28672), (65, 1000, 8192)):
+    # prefill m: the split that fills the 256 CUs in the fewest rounds per unit of work
+    for (m, N, K), S in (((256, 8192, 8192), 4), ((256, 10240, 8192), 3), ((256, 8192, 28672), 4),
+                         ((65, 1000, 8192), 8)):
         b = F.workspace_size(m, N, K, 0)
-        assert b % (4 * m * N) == 0 and b // (4 * m * N) in (0, 2, 4, 8)
+        assert b == S * 4 * m * N, (m, N, K, b)
     assert F.workspace_size(256, 57344, 8192, 0) == 0
     assert F.new_workspace(1000, 57344, 8192, 0) is None
 

@@ -1,5 +1,7 @@
 /*
- * fp4gemm.h -- C ABI of the BF16 / FP16 x FP4 block-scaled GEMM for AMD MI355X (gfx950).
+ * fp4gemm.h -- C ABI of the BF16 / FP16 x FP4 block-scaled GEMM for AMD MI355X (gfx950),
+ * with its grouped mixture-of-experts variant, the offline repack and the
+ * offline quantizer.
  *
  *   Y[m][N] = A[m][K] . dequant(W)[N][K]^T,   dequant(W)[n][k] = e2m1(code[n][k]) * scale[n][k / G]
  *
@@ -33,7 +35,8 @@
  *   - Every argument check happens before any HIP call.  A failed check
  *     leaves every output untouched.
  *   - The caller owns every buffer.  The library never allocates, frees or
- *     synchronizes inside fp4_gemm / fp4_dequant.
+ *     synchronizes in any device entry (fp4_gemm*, fp4_moe_gemm,
+ *     fp4_quantize, fp4_dequant*): they only queue kernels on `stream`.
  *   - "device" pointers must be HIP device memory on the current device;
  *     "host" pointers must be ordinary host memory.
  *   - Functions are reentrant and thread-safe; the only global state is a
@@ -60,9 +63,11 @@ enum {
     FP4_OK = 0,
     FP4_ERR_NULL = 1,      /* a required pointer is NULL */
     FP4_ERR_SHAPE = 2,     /* N < 1, K < G, K % G != 0, m < 0, a size over the limits below,
-                              or (fp4_gemm) a device pointer not 16-byte aligned */
-    FP4_ERR_FORMAT = 3,    /* format is neither FP4_NVFP4 nor FP4_MXFP4 */
-    FP4_ERR_VALUE = 4,     /* fp4_repack: a scale byte is negative or NaN */
+                              or a device pointer not aligned as its entry requires */
+    FP4_ERR_FORMAT = 3,    /* format is neither FP4_NVFP4 nor FP4_MXFP4 (or, fp4_gemm_ex, an
+                              activation type other than 0 / 1) */
+    FP4_ERR_VALUE = 4,     /* fp4_repack: a scale byte is negative or NaN; fp4_gemm_ex /
+                              fp4_quantize: alpha outside its documented range */
     FP4_ERR_WORKSPACE = 5, /* workspace smaller than fp4_gemm_workspace_size */
     FP4_ERR_DEVICE = 6,    /* no current HIP device, or it is not gfx950 */
     FP4_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed */

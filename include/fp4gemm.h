@@ -192,6 +192,46 @@ int fp4_gemm_ex(const void* A, const void* wq, const void* sq, void* C, int64_t 
 int fp4_quantize(const void* W, void* codes, void* scales, int64_t N, int64_t K, int format, float alpha,
                  void* stream);
 
+/* ---- Native FP4 path (FP4 x FP4 on the gfx950 matrix cores) ----------------
+ * The Petit blog's introduction: MI350 multiplies FP4 natively.  Unlike the
+ * entries above, this path quantizes the activations: each 32-element K block
+ * of every row of A becomes MXFP4 by the fp4_quantize rule (alpha 1), and the
+ * product of the two MXFP4 operands is accumulated in FP32:
+ *     C = alpha * (dequant(quantize(A)) . dequant(W)^T)
+ * MXFP4 weights only (the matrix core's block scale is E8M0 per 32), in their
+ * own packed layout (fp4_native_repack). */
+
+/* Bytes of the native packed codes and scales (the MXFP4 sizes of
+ * fp4_repack_size). */
+int fp4_native_repack_size(int64_t N, int64_t K, size_t* wq_bytes, size_t* sq_bytes);
+
+/* Offline, host to host: canonical MXFP4 codes [N][K/2] and scales [N][K/32]
+ * -> the native packed layout (a pure permutation plus zero padding; scale
+ * byte 0xFF rejected with FP4_ERR_VALUE, nothing written then). */
+int fp4_native_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, uint8_t* wq,
+                      uint8_t* sq);
+
+/* Exact inverse of fp4_native_repack (host to host). */
+int fp4_native_unpack(const uint8_t* wq, const uint8_t* sq, int64_t N, int64_t K, uint8_t* codes,
+                      uint8_t* scales);
+
+/* Workspace of fp4_gemm_native: the quantized activations (m x Kp/2 code
+ * bytes and m x Kp/32 scale bytes, Kp = K rounded up to 512) plus FP32
+ * partials when K is split; 0 for m == 0. */
+int fp4_gemm_native_workspace_size(int64_t m, int64_t N, int64_t K, size_t* bytes);
+
+/* C = alpha * (dequant(quantize(A)) . dequant(W)^T) on `stream`:
+ *   A  device BF16 [m][K]; wq / sq from fp4_native_repack (device);
+ *   C  device BF16 [m][N], every element written; alpha as fp4_gemm_ex;
+ *   workspace: device, 256-byte aligned, at least
+ *   fp4_gemm_native_workspace_size bytes (FP4_ERR_WORKSPACE otherwise);
+ *   its contents are scratch.  A, wq, sq and C 16-byte aligned.
+ * K % 32 == 0, m <= 2^20, m * Kp / 2 and m * N * 2 below 2^31 (else
+ * FP4_ERR_SHAPE).  Two kernels (activation quantizer, FP4 GEMM; a third sums
+ * the K-split partials); deterministic. */
+int fp4_gemm_native(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
+                    float alpha, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Grouped mixture-of-experts GEMM with BF16 activations (the petit-kernel
  * page, "Features": fused MoE kernels for BF16 and MXFP4 workloads; both FP4
  * formats are accepted).  For expert e = 0 .. E-1 and every assignment id

@@ -358,16 +358,112 @@ static int quantize_impl(const void* W, void* codes, void* scales, int64_t N, in
     const dim3 grid((unsigned)((groups + 255) / 256)), block(256);
     if (format == FP4_NVFP4)
         quantize_kernel<0><<<grid, block, 0, s>>>((const uint16_t*)W, (uint8_t*)codes, (uint8_t*)scales, groups,
-                                                  alpha);
+                                                  alpha, K / G, K / G);
     else
         quantize_kernel<1><<<grid, block, 0, s>>>((const uint16_t*)W, (uint8_t*)codes, (uint8_t*)scales, groups,
-                                                  alpha);
+                                                  alpha, K / G, K / G);
+    return launch_status();
+}
+
+// Native FP4 path: workspace = quantized activations (m rows of Kp / 2 code
+// bytes, then m rows of Kp / 32 scale bytes, 256-byte aligned) + FP32
+// partials of a K split.  K split: the largest S <= 8 (and <= Kp / 512) that
+// keeps blocks * S within one round of 256 workgroups.
+// Native kernel shape: 0 = four waves of 4 m-blocks x 2 n-tiles (BM 64, BN
+// 128), 1 = four waves of 8 m-blocks x 1 n-tile (BM 128, BN 64);
+// FP4GEMM_NATIVE=0|1 overrides the default (0).
+static int native_shape_id() {
+    static const int id = [] {
+        const char* e = getenv("FP4GEMM_NATIVE");
+        return e && e[0] == '1' ? 1 : 0;
+    }();
+    return id;
+}
+static int native_bm() { return native_shape_id() == 0 ? 64 : 128; }
+static int native_bnt() { return native_shape_id() == 0 ? 8 : 4; }
+
+struct NativePlan {
+    int64_t codes_bytes, scales_off, scales_bytes, partial_off;
+    int S;
+    size_t total;
+};
+static NativePlan native_plan(int64_t m, int64_t N, int64_t K) {
+    NativePlan p{};
+    const int64_t Kp = padded_k(K), QB = Kp / kScaleBlockK, NT = padded_n(N) / kTileN;
+    p.codes_bytes = m * Kp / 2;
+    p.scales_off = round_up(p.codes_bytes, 256);
+    p.scales_bytes = m * Kp / 32;
+    p.partial_off = round_up(p.scales_off + p.scales_bytes, 256);
+    const int64_t blocks = ((m + native_bm() - 1) / native_bm()) * ((NT + native_bnt() - 1) / native_bnt());
+    p.S = 1;
+    while (p.S < 8 && 2 * p.S <= QB && blocks * 2 * p.S <= kCUs) p.S *= 2;
+    p.total = size_t(p.partial_off) + (p.S > 1 ? size_t(p.S) * size_t(m) * size_t(N) * 4 : 0);
+    return p;
+}
+
+static int native_check(int64_t m, int64_t N, int64_t K) {
+    int st = fp4_check_weight_shape(N, K, FP4_MXFP4);
+    if (st != FP4_OK) return st;
+    if (m < 0 || m > (int64_t(1) << 20)) return FP4_ERR_SHAPE;
+    if (round_up(m, 128) * padded_k(K) / 2 >= (int64_t(1) << 31) || round_up(m, 128) * N * 2 >= (int64_t(1) << 31))
+        return FP4_ERR_SHAPE;
+    return FP4_OK;
+}
+
+static int native_impl(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
+                       float alpha, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = native_check(m, N, K);
+    if (st != FP4_OK) return st;
+    if (!alpha_ok(alpha)) return FP4_ERR_VALUE;
+    if (m == 0) return FP4_OK;
+    if (!A || !wq || !sq || !C) return FP4_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(wq) | reinterpret_cast<uintptr_t>(sq) |
+         reinterpret_cast<uintptr_t>(C)) & 15)
+        return FP4_ERR_SHAPE;
+    const NativePlan p = native_plan(m, N, K);
+    if (!workspace || workspace_bytes < p.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+        return FP4_ERR_WORKSPACE;
+    st = check_device();
+    if (st != FP4_OK) return st;
+    const int64_t Kp = padded_k(K), Np = padded_n(N);
+    const int KB = int(Kp / kChunkK), NT = int(Np / kTileN);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* aq = ws;
+    uint8_t* as = ws + p.scales_off;
+    float* P = p.S > 1 ? reinterpret_cast<float*>(ws + p.partial_off) : nullptr;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const int64_t groups = m * (Kp / 32);
+    quantize_kernel<1><<<dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s>>>(
+        (const uint16_t*)A, aq, as, groups, 1.0f, K / 32, Kp / 32);
+    const int MT = int((m + native_bm() - 1) / native_bm()), NG = (NT + native_bnt() - 1) / native_bnt();
+    const dim3 grid(MT * NG * p.S), block(256);
+    if (native_shape_id() == 0)
+        gemm_native<1, 4, 4, 2><<<grid, block, 0, s>>>(aq, as, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, P,
+                                                       int(m), int(N), KB, NT, p.S, alpha);
+    else
+        gemm_native<1, 4, 8, 1><<<grid, block, 0, s>>>(aq, as, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, P,
+                                                       int(m), int(N), KB, NT, p.S, alpha);
+    if (P) launch_reduce(0, P, C, m * N, p.S, alpha, s);
     return launch_status();
 }
 
 }  // namespace fp4
 
 using namespace fp4;
+
+extern "C" int fp4_gemm_native_workspace_size(int64_t m, int64_t N, int64_t K, size_t* bytes) {
+    int st = native_check(m, N, K);
+    if (st != FP4_OK) return st;
+    if (!bytes) return FP4_ERR_NULL;
+    *bytes = m == 0 ? 0 : native_plan(m, N, K).total;
+    return FP4_OK;
+}
+
+extern "C" int fp4_gemm_native(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
+                               float alpha, void* workspace, size_t workspace_bytes, void* stream) {
+    return native_impl(A, wq, sq, C, m, N, K, alpha, workspace, workspace_bytes, stream);
+}
 
 extern "C" int fp4_gemm_ex(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
                            int format, int act_type, float alpha, void* workspace, size_t workspace_bytes,

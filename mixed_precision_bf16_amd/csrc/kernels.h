@@ -846,13 +846,24 @@ __device__ __forceinline__ float e4m3_decode(uint32_t byte) {
 }
 
 template <int FMT>
+// Output rows hold gpr_out >= gpr_in blocks: blocks past the input row's
+// gpr_in are written as zero blocks (codes 0, scale byte 0), which pads K for
+// the native FP4 path; gpr_out == gpr_in is the canonical layout.
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ W, uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales, int64_t groups, float alpha) {
+                                                       uint8_t* __restrict__ scales, int64_t groups, float alpha,
+                                                       int64_t gpr_in, int64_t gpr_out) {
     constexpr int G = FMT == 0 ? 16 : 32;
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (g >= groups) return;
+    const int64_t row = g / gpr_out, blk = g - row * gpr_out;
+    if (blk >= gpr_in) {
+        if constexpr (FMT == 0) *reinterpret_cast<u32x2*>(codes + g * (G / 2)) = u32x2{0u, 0u};
+        else *reinterpret_cast<u32x4*>(codes + g * (G / 2)) = u32x4{0u, 0u, 0u, 0u};
+        scales[g] = 0;
+        return;
+    }
     u32x4 v[G / 8];
-    const u32x4* src = reinterpret_cast<const u32x4*>(W + g * G);
+    const u32x4* src = reinterpret_cast<const u32x4*>(W + (row * gpr_in + blk) * G);
 #pragma unroll
     for (int i = 0; i < G / 8; ++i) v[i] = src[i];
     float x[G];
@@ -914,6 +925,186 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
         *reinterpret_cast<u32x4*>(codes + g * (G / 2)) = u32x4{out[0], out[1], out[2], out[3]};
     }
     scales[g] = (uint8_t)sb;
+}
+
+// ------------------------------------------------------------ native FP4 GEMM
+// The FP4 matrix-core path of gfx950 (the Petit blog's introduction: MI350
+// multiplies FP4 natively).  Both operands are MXFP4: the weights in the
+// native layout (fp4_native_repack; one 1 KiB block per 16-row tile and
+// 128-K chunk, one 256-byte scale block per tile and 512 K), the activations
+// quantized to MXFP4 by quantize_kernel<1> into rows of Kp / 2 code bytes
+// and Kp / 32 scale bytes (K zero-padded to Kp = 512 multiple).  One
+// v_mfma_scale_f32_16x16x128_f8f6f4 per (tile, m-block, chunk) multiplies
+// 16 x 128 FP4 weights by 16 x 128 FP4 activations with one E8M0 scale per
+// lane and operand (lane l = 16 j + r: row r, k = 32 j .. 32 j + 31 of the
+// chunk; the weight scale is byte (chunk % 4) of the lane's scale dword, the
+// activation scale the low byte after shifting by 8 j).
+// Workgroup: four waves, WN n-groups x WM m-groups, a wave owns MBW m-blocks
+// and TNW n-tiles; the activation chunk (BM rows x 64 code bytes + 4 scale
+// bytes per row) goes through registers into a double-buffered LDS tile one
+// chunk ahead; the code blocks stream three chunks ahead in a four-slot
+// register ring; K split over S workgroups as in the prefill kernel.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int WM, int WN, int MBW, int TNW>
+__global__ __launch_bounds__(256) void gemm_native(const uint8_t* __restrict__ Aq, const uint8_t* __restrict__ As,
+                                                  const u32x4* __restrict__ wq, const uint8_t* __restrict__ sq,
+                                                  uint16_t* __restrict__ C, float* __restrict__ P, int M, int N,
+                                                  int KB, int NT, int S, float alpha) {
+    static_assert(WM * WN == 4, "four waves");
+    constexpr int BM = WM * MBW * 16;
+    constexpr int BNT = WN * TNW;
+    constexpr int kCodeBuf = BM * 64;               // one chunk of activation codes
+    constexpr int kBuf = kCodeBuf + BM * 4;         // plus its scale bytes
+    constexpr int kPieces = BM * 4 / 256;           // 16-byte code pieces per thread per chunk
+    static_assert(kPieces >= 1 && BM * 4 % 256 == 0, "whole pieces");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, j = lane >> 4;
+    const int wm = wave % WM, wn = wave / WM;
+    const int MT = (M + BM - 1) / BM, NG = (NT + BNT - 1) / BNT;
+    const int ks = blockIdx.x % S, item = blockIdx.x / S;
+    const int total = MT * NG;
+    int L = item;
+    if (total % kXcdCount == 0 && S == 1) L = (item % kXcdCount) * (total / kXcdCount) + item / kXcdCount;
+    const int mt = L % MT, ng = L / MT;
+    const int m0 = mt * BM, tile0 = ng * BNT + wn * TNW;
+    const int QB = KB / 4;                          // 512-K groups
+    const int q0 = (ks * QB) / S, q1 = ((ks + 1) * QB) / S;
+    const int c0 = 4 * q0, clast = 4 * q1 - 1;
+    const int row_bytes = KB * 64, srow_bytes = KB * 4;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Aq, (uint32_t)(M * row_bytes));
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As, (uint32_t)(M * srow_bytes));
+    __amdgpu_buffer_rsrc_t rw[TNW], rs[TNW];
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt) {
+        const int t = min(tile0 + tt, NT - 1);
+        rw[tt] = make_rsrc(reinterpret_cast<const uint8_t*>(wq) + (size_t)t * KB * 1024, (uint32_t)KB * 1024u);
+        rs[tt] = make_rsrc(sq + (size_t)t * QB * 256, (uint32_t)QB * 256u);
+    }
+
+    // activation staging: code piece p of this thread = (row, 16-byte column
+    // of the chunk's 64 bytes); threads 0 .. BM-1 also bring the row's 4 scale bytes
+    u32x4 st[kPieces];
+    uint32_t sst = 0;
+    auto a_issue = [&](int chunk) {
+        chunk = min(chunk, clast);
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) {
+            const int idx = tid + 256 * p, row = idx >> 2, col = idx & 3;
+            st[p] = __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)((m0 + row) * row_bytes + chunk * 64 + col * 16),
+                                                          0, 0);
+        }
+        if (tid < BM) sst = __builtin_amdgcn_raw_buffer_load_b32(rsa, (uint32_t)((m0 + tid) * srow_bytes + chunk * 4),
+                                                                  0, 0);
+    };
+    auto a_store = [&](int buf) {
+        uint8_t* base = lds + buf * kBuf;
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) *reinterpret_cast<u32x4*>(base + (tid + 256 * p) * 16) = st[p];
+        if (tid < BM) *reinterpret_cast<uint32_t*>(base + kCodeBuf + tid * 4) = sst;
+    };
+    u32x4 wr[4][TNW];
+    auto w_issue = [&](auto slot_c, int chunk) {
+        constexpr int SL = decltype(slot_c)::value;
+        chunk = min(chunk, clast);
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt)
+            wr[SL][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, kLoadStream);
+    };
+    auto lds_barrier = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    f32x4 acc[TNW][MBW];
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // chunk at position T (0..3) of its 512-K group, activations in LDS buffer buf
+    auto compute = [&](auto t_c, int buf, const uint32_t (&wsc)[TNW]) {
+        constexpr int T = decltype(t_c)::value;
+        const uint8_t* base = lds + buf * kBuf;
+        i32x8 a[MBW];
+        int asc[MBW];
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+            const int row = wm * MBW * 16 + mb * 16 + r;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(base + row * 64 + j * 16);
+            a[mb] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            asc[mb] = (int)(*reinterpret_cast<const uint32_t*>(base + kCodeBuf + row * 4) >> (8 * j));
+        }
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt) {
+            const u32x4 w = wr[T][tt];
+            const i32x8 b = i32x8{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb)
+                acc[tt][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a[mb], acc[tt][mb], 4, 4, T,
+                                                                               (int)wsc[tt], 0, asc[mb]);
+        }
+    };
+    uint32_t sa[TNW], sb[TNW];
+    auto group = [&](int q, const uint32_t (&cur)[TNW], uint32_t (&nxt)[TNW]) {
+        const int base = 4 * q;
+        const int nq = min(q + 1, q1 - 1);
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt)
+            nxt[tt] = __builtin_amdgcn_raw_buffer_load_b32(rs[tt], lane * 4, nq * 256, kLoadStream);
+        auto step = [&](auto t_c) {
+            constexpr int T = decltype(t_c)::value;
+            a_issue(base + T + 1);
+            w_issue(std::integral_constant<int, (T + 3) % 4>{}, base + T + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(t_c, T % 2, cur);
+            __builtin_amdgcn_sched_barrier(0);
+            a_store((T + 1) % 2);
+            lds_barrier();
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+    };
+
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt) sa[tt] = __builtin_amdgcn_raw_buffer_load_b32(rs[tt], lane * 4, q0 * 256, kLoadStream);
+    a_issue(c0);
+    w_issue(std::integral_constant<int, 0>{}, c0);
+    w_issue(std::integral_constant<int, 1>{}, c0 + 1);
+    w_issue(std::integral_constant<int, 2>{}, c0 + 2);
+    a_store(0);
+    lds_barrier();
+    int q = q0;
+    for (; q + 1 < q1; q += 2) {
+        group(q, sa, sb);
+        group(q + 1, sb, sa);
+    }
+    if (q < q1) group(q, sa, sb);
+
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+            const int m = m0 + wm * MBW * 16 + mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
+            if (P == nullptr) {
+                store_frag<0>(C, acc[tt][mb] * alpha, m, n0, M, N);
+            } else if (m < M) {
+                float* dst = P + ((size_t)ks * M + m) * N + n0;
+                if ((N & 3) == 0 && n0 + 3 < N) {
+                    *reinterpret_cast<f32x4*>(dst) = acc[tt][mb];
+                } else {
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + e < N) dst[e] = acc[tt][mb][e];
+                }
+            }
+        }
 }
 
 // ------------------------------------------------------------ debug dequant

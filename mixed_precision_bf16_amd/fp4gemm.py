@@ -40,6 +40,12 @@ _SIGNATURES = {
     "fp4_gemm_ex": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_float, _c_vp, _c_sz, _c_vp]),
     "fp4_quantize": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, ctypes.c_float, _c_vp]),
+    "fp4_native_repack_size": (ctypes.c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz), ctypes.POINTER(_c_sz)]),
+    "fp4_native_repack": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
+    "fp4_native_unpack": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
+    "fp4_gemm_native_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fp4_gemm_native": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_vp,
+                                       _c_sz, _c_vp]),
     "fp4_moe_gemm": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                     _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
 }
@@ -257,5 +263,59 @@ def moe_gemm(A, wq, sq, sorted_ids, expert_offsets, N: int, K: int, fmt: int, E:
     _check(lib().fp4_moe_gemm(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(sorted_ids), _dev_ptr(expert_offsets),
                               _dev_ptr(topk_weights), _dev_ptr(out), A.shape[0], a_div, out_rows,
                               sorted_ids.numel(), E, N, K, fmt, _stream_handle(stream)), "fp4_moe_gemm")
+    return out
+
+
+def native_repack(codes, scales, N: int, K: int):
+    """fp4_native_repack: canonical MXFP4 codes / scales (host, uint8) -> native
+    packed (wq, sq) as CPU uint8 tensors."""
+    import numpy as np
+    import torch
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    if codes.size != N * K // 2 or scales.size != N * (K // 32):
+        raise ValueError("codes / scales have the wrong size")
+    wqb, sqb = _c_sz(), _c_sz()
+    _check(lib().fp4_native_repack_size(N, K, ctypes.byref(wqb), ctypes.byref(sqb)), "fp4_native_repack_size")
+    wq = np.empty(wqb.value, np.uint8)
+    sq = np.empty(sqb.value, np.uint8)
+    _check(lib().fp4_native_repack(codes.ctypes.data_as(_c_vp), scales.ctypes.data_as(_c_vp), N, K,
+                                   wq.ctypes.data_as(_c_vp), sq.ctypes.data_as(_c_vp)), "fp4_native_repack")
+    return torch.from_numpy(wq), torch.from_numpy(sq)
+
+
+def native_unpack(wq, sq, N: int, K: int):
+    """Inverse of native_repack (host arrays or CPU tensors) -> (codes, scales) numpy."""
+    import numpy as np
+    wq = np.ascontiguousarray(wq.numpy() if hasattr(wq, "numpy") else wq, dtype=np.uint8)
+    sq = np.ascontiguousarray(sq.numpy() if hasattr(sq, "numpy") else sq, dtype=np.uint8)
+    codes = np.empty((N, K // 2), np.uint8)
+    scales = np.empty((N, K // 32), np.uint8)
+    _check(lib().fp4_native_unpack(wq.ctypes.data_as(_c_vp), sq.ctypes.data_as(_c_vp), N, K,
+                                   codes.ctypes.data_as(_c_vp), scales.ctypes.data_as(_c_vp)), "fp4_native_unpack")
+    return codes, scales
+
+
+def native_workspace_size(m: int, N: int, K: int) -> int:
+    b = _c_sz()
+    _check(lib().fp4_gemm_native_workspace_size(m, N, K, ctypes.byref(b)), "fp4_gemm_native_workspace_size")
+    return b.value
+
+
+def gemm_native(A, wq, sq, N: int, K: int, out=None, workspace=None, stream=None, alpha: float = 1.0):
+    """fp4_gemm_native: C = alpha * dequant(quantize_mxfp4(A)) . dequant(W)^T
+    with W in the native layout; A bfloat16 CUDA [m][K]."""
+    import torch
+    if A.dtype != torch.bfloat16 or A.dim() != 2 or not A.is_cuda or not A.is_contiguous() or A.shape[1] != K:
+        raise ValueError("A must be a contiguous bfloat16 CUDA tensor [m][K]")
+    m = A.shape[0]
+    if out is None:
+        out = torch.empty((m, N), dtype=torch.bfloat16, device=A.device)
+    need = native_workspace_size(m, N, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().fp4_gemm_native(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), m, N, K, alpha,
+                                 _dev_ptr(workspace), ws_bytes, _stream_handle(stream)), "fp4_gemm_native")
     return out
 

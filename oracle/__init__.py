@@ -30,4 +30,4 @@ from .fp4_oracle import (  # noqa: F401
     unpack_codes,
 )
 from .moe_oracle import moe_reference  # noqa: F401,E402
-from .quant_oracle import quantize_reference, scaled_gemm_reference  # noqa: F401,E402
+from .quant_oracle import native_reference, quantize_reference, scaled_gemm_reference  # noqa: F401,E402

@@ -110,3 +110,16 @@ def scaled_gemm_reference(y_ref: np.ndarray, bound: np.ndarray, alpha: float):
     """Y = alpha * (A . dequant(W)^T); the bound scales the same way."""
     a = float(np.float32(alpha))
     return a * y_ref, abs(a) * bound
+
+
+def native_reference(a_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, K: int):
+    """The native FP4 path (FP4 x FP4 on the matrix cores; the Petit blog's
+    introduction: MI350 multiplies FP4 natively): the activations are
+    quantized to MXFP4 by the quantizer above (alpha 1), then
+    Y = dequant(quantize(A)) . dequant(W)^T and B = |.| . |.|^T in float64,
+    with MXFP4 weights.  Returns (y_ref, bound)."""
+    from .fp4_oracle import dequant_weights
+    qc, qs = quantize_reference(a_bits, 1, 1.0)
+    a = dequant_weights(qc, qs, K, 1)
+    w = dequant_weights(codes, scales, K, 1)
+    return a @ w.T, np.abs(a) @ np.abs(w).T

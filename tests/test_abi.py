@@ -226,6 +226,47 @@ def test_gemm_ex_and_quantize_argument_errors_before_any_hip_call():
         assert q(d, d, d, 4, 64, 0, bad, None) == 4, bad
 
 
+def test_native_repack_roundtrip_and_layout():
+    rng = np.random.Generator(np.random.PCG64(12))
+    for N, K in ((5, 64), (37, 2880), (16, 512), (130, 1056)):
+        codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+        scales = rng.integers(0, 255, size=(N, K // 32), dtype=np.uint8)
+        wq, sq = F.native_repack(codes, scales, N, K)
+        nw, ns = F.repack_size(N, K, F.MXFP4)
+        assert wq.numel() == nw and sq.numel() == ns
+        c2, s2 = F.native_unpack(wq, sq, N, K)
+        assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+        wqn, sqn = wq.numpy(), sq.numpy()
+        KB, QB = -(-K // 512) * 4, -(-K // 512)
+        for _ in range(20):                      # documented offsets
+            n, kb = int(rng.integers(N)), int(rng.integers(K // 32))
+            t, r, c, j = n // 16, n % 16, kb // 4, kb % 4
+            off = (t * KB + c) * 1024 + (16 * j + r) * 16
+            assert bytes(wqn[off:off + 16]) == bytes(codes[n, kb * 16:kb * 16 + 16])
+            q, s_ = kb // 16, (kb % 16) // 4
+            assert sqn[(t * QB + q) * 256 + (16 * j + r) * 4 + s_] == scales[n, kb]
+    lib = F.lib()
+    d = ctypes.c_void_p(16)
+    z = ctypes.c_void_p(0)
+    assert lib.fp4_native_repack(z, d, 4, 64, d, d) == 1
+    assert lib.fp4_native_repack(d, d, 4, 48, d, d) == 2                     # K % 32
+    bad = np.full((2, 2), 0xFF, np.uint8)
+    buf = np.zeros(4096, np.uint8)
+    assert lib.fp4_native_repack(np.zeros((2, 32), np.uint8).ctypes.data_as(ctypes.c_void_p),
+                                 bad.ctypes.data_as(ctypes.c_void_p), 2, 64, buf.ctypes.data_as(ctypes.c_void_p),
+                                 buf.ctypes.data_as(ctypes.c_void_p)) == 4
+    g = lib.fp4_gemm_native
+    assert g(d, d, d, d, 16, 64, 48, 1.0, d, 1 << 20, None) == 2
+    assert g(d, d, d, d, 16, 64, 64, float("nan"), d, 1 << 20, None) == 4
+    assert g(z, z, z, z, 0, 64, 64, 1.0, None, 0, None) == 0
+    assert g(z, d, d, d, 16, 64, 64, 1.0, d, 1 << 20, None) == 1
+    assert g(d, d, d, d, 16, 64, 64, 1.0, ctypes.c_void_p(272), 1 << 20, None) == 5      # workspace alignment
+    assert g(d, d, d, d, 16, 64, 64, 1.0, d, 16, None) == 5                            # workspace size
+    sz = ctypes.c_size_t(0)
+    assert lib.fp4_gemm_native_workspace_size(256, 57344, 8192, ctypes.byref(sz)) == 0
+    assert sz.value >= 256 * 8192 // 2 + 256 * 8192 // 32
+
+
 def test_python_binding_validation():
     codes, scales = _rand_weights(4, 64, 0, 1)
     with pytest.raises(ValueError):

@@ -128,6 +128,30 @@ def test_alpha_scales_output_and_scales():
     assert np.array_equal(O.e4m3_value(s2), 2 * O.e4m3_value(s1))
 
 
+def test_native_reference_equals_dense_on_representable_activations():
+    """Activations that are exact MXFP4 values (code x 2^e with a full-range
+    block maximum) quantize to themselves (the fixed-point pin), so the
+    native reference must equal the pinned dense reference exactly; on
+    general activations it must differ (it quantizes)."""
+    rng = np.random.Generator(np.random.PCG64(6))
+    m, N, K = 5, 7, 128
+    acodes = rng.integers(0, 16, size=(m, K)).astype(np.uint8)
+    acodes[acodes == 8] = 0
+    acodes[:, ::32] = 7
+    apacked = (acodes[:, 0::2] | (acodes[:, 1::2] << 4)).astype(np.uint8)
+    ascales = rng.integers(120, 134, size=(m, K // 32)).astype(np.uint8)
+    a_bits = O.bf16_bits_of_exact(O.dequant_weights(apacked, ascales, K, 1))
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(120, 134, size=(N, K // 32)).astype(np.uint8)
+    y, b = O.gemm_reference(a_bits, codes, scales, K, 1)
+    yn, bn = Q.native_reference(a_bits, codes, scales, K)
+    assert np.array_equal(y, yn) and np.array_equal(b, bn)
+    g = _bf16_bits(rng.standard_normal((m, K)).astype(np.float32))
+    y, _ = O.gemm_reference(g, codes, scales, K, 1)
+    yn, _ = Q.native_reference(g, codes, scales, K)
+    assert not np.array_equal(y, yn)
+
+
 class _Mut:
     def __init__(self, **over):
         self.__dict__.update({k: getattr(Q, k) for k in ("e4m3_rne_byte", "nearest_e2m1", "quantize_reference")})

@@ -369,18 +369,10 @@ static int quantize_impl(const void* W, void* codes, void* scales, int64_t N, in
 // bytes, then m rows of Kp / 32 scale bytes, 256-byte aligned) + FP32
 // partials of a K split.  K split: the largest S <= 8 (and <= Kp / 512) that
 // keeps blocks * S within one round of 256 workgroups.
-// Native kernel shape: 0 = four waves of 4 m-blocks x 2 n-tiles (BM 64, BN
-// 128), 1 = four waves of 8 m-blocks x 1 n-tile (BM 128, BN 64);
-// FP4GEMM_NATIVE=0|1 overrides the default (0).
-static int native_shape_id() {
-    static const int id = [] {
-        const char* e = getenv("FP4GEMM_NATIVE");
-        return e && e[0] == '1' ? 1 : 0;
-    }();
-    return id;
-}
-static int native_bm() { return native_shape_id() == 0 ? 64 : 128; }
-static int native_bnt() { return native_shape_id() == 0 ? 8 : 4; }
+// Native kernel shape: four waves of 4 m-blocks x 2 n-tiles (BM 64, BN 128;
+// 357 VGPRs).  Eight m-blocks per wave do not fit the registers.
+static int native_bm() { return 64; }
+static int native_bnt() { return 8; }
 
 struct NativePlan {
     int64_t codes_bytes, scales_off, scales_bytes, partial_off;
@@ -438,12 +430,8 @@ static int native_impl(const void* A, const void* wq, const void* sq, void* C, i
         (const uint16_t*)A, aq, as, groups, 1.0f, K / 32, Kp / 32);
     const int MT = int((m + native_bm() - 1) / native_bm()), NG = (NT + native_bnt() - 1) / native_bnt();
     const dim3 grid(MT * NG * p.S), block(256);
-    if (native_shape_id() == 0)
-        gemm_native<1, 4, 4, 2><<<grid, block, 0, s>>>(aq, as, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, P,
-                                                       int(m), int(N), KB, NT, p.S, alpha);
-    else
-        gemm_native<1, 4, 8, 1><<<grid, block, 0, s>>>(aq, as, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, P,
-                                                       int(m), int(N), KB, NT, p.S, alpha);
+    gemm_native<1, 4, 4, 2><<<grid, block, 0, s>>>(aq, as, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, P,
+                                                   int(m), int(N), KB, NT, p.S, alpha);
     if (P) launch_reduce(0, P, C, m * N, p.S, alpha, s);
     return launch_status();
 }

@@ -940,9 +940,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
 // chunk; the weight scale is byte (chunk % 4) of the lane's scale dword, the
 // activation scale the low byte after shifting by 8 j).
 // Workgroup: four waves, WN n-groups x WM m-groups, a wave owns MBW m-blocks
-// and TNW n-tiles; the activation chunk (BM rows x 64 code bytes + 4 scale
-// bytes per row) goes through registers into a double-buffered LDS tile one
-// chunk ahead; the code blocks stream three chunks ahead in a four-slot
+// and TNW n-tiles.  The activations of one 512-K group (four chunks: BM rows x
+// 256 code bytes + 16 scale bytes per row) go through registers into a
+// double-buffered LDS tile one group ahead (one barrier per group; the
+// 16-byte code slots are XOR-swizzled by row, so fragment reads are free of
+// bank conflicts); the code blocks stream three chunks ahead in a four-slot
 // register ring; K split over S workgroups as in the prefill kernel.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -954,10 +956,10 @@ __global__ __launch_bounds__(256) void gemm_native(const uint8_t* __restrict__ A
     static_assert(WM * WN == 4, "four waves");
     constexpr int BM = WM * MBW * 16;
     constexpr int BNT = WN * TNW;
-    constexpr int kCodeBuf = BM * 64;               // one chunk of activation codes
-    constexpr int kBuf = kCodeBuf + BM * 4;         // plus its scale bytes
-    constexpr int kPieces = BM * 4 / 256;           // 16-byte code pieces per thread per chunk
-    static_assert(kPieces >= 1 && BM * 4 % 256 == 0, "whole pieces");
+    constexpr int kCodeBuf = BM * 256;              // one 512-K group of activation codes
+    constexpr int kBuf = kCodeBuf + BM * 16;        // plus its scale bytes
+    constexpr int kPieces = BM * 16 / 256;          // 16-byte code pieces per thread per group
+    static_assert(kPieces >= 1 && BM * 16 % 256 == 0 && BM <= 256, "whole pieces");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -973,7 +975,7 @@ __global__ __launch_bounds__(256) void gemm_native(const uint8_t* __restrict__ A
     const int m0 = mt * BM, tile0 = ng * BNT + wn * TNW;
     const int QB = KB / 4;                          // 512-K groups
     const int q0 = (ks * QB) / S, q1 = ((ks + 1) * QB) / S;
-    const int c0 = 4 * q0, clast = 4 * q1 - 1;
+    const int clast = 4 * q1 - 1;
     const int row_bytes = KB * 64, srow_bytes = KB * 4;
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(Aq, (uint32_t)(M * row_bytes));
@@ -986,26 +988,30 @@ __global__ __launch_bounds__(256) void gemm_native(const uint8_t* __restrict__ A
         rs[tt] = make_rsrc(sq + (size_t)t * QB * 256, (uint32_t)QB * 256u);
     }
 
-    // activation staging: code piece p of this thread = (row, 16-byte column
-    // of the chunk's 64 bytes); threads 0 .. BM-1 also bring the row's 4 scale bytes
+    // staging: code piece p of this thread = (row, 16-byte slot s of the
+    // group's 256 bytes: chunk s / 4, lane group s % 4); threads 0 .. BM-1
+    // also bring their row's 16 scale bytes
     u32x4 st[kPieces];
-    uint32_t sst = 0;
-    auto a_issue = [&](int chunk) {
-        chunk = min(chunk, clast);
+    u32x4 sst = u32x4{0u, 0u, 0u, 0u};
+    auto a_issue = [&](int q) {
+        q = min(q, q1 - 1);
 #pragma unroll
         for (int p = 0; p < kPieces; ++p) {
-            const int idx = tid + 256 * p, row = idx >> 2, col = idx & 3;
-            st[p] = __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)((m0 + row) * row_bytes + chunk * 64 + col * 16),
+            const int idx = tid + 256 * p, row = idx >> 4, slot = idx & 15;
+            st[p] = __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)((m0 + row) * row_bytes + q * 256 + slot * 16),
                                                           0, 0);
         }
-        if (tid < BM) sst = __builtin_amdgcn_raw_buffer_load_b32(rsa, (uint32_t)((m0 + tid) * srow_bytes + chunk * 4),
-                                                                  0, 0);
+        if (tid < BM)
+            sst = __builtin_amdgcn_raw_buffer_load_b128(rsa, (uint32_t)((m0 + tid) * srow_bytes + q * 16), 0, 0);
     };
     auto a_store = [&](int buf) {
         uint8_t* base = lds + buf * kBuf;
 #pragma unroll
-        for (int p = 0; p < kPieces; ++p) *reinterpret_cast<u32x4*>(base + (tid + 256 * p) * 16) = st[p];
-        if (tid < BM) *reinterpret_cast<uint32_t*>(base + kCodeBuf + tid * 4) = sst;
+        for (int p = 0; p < kPieces; ++p) {
+            const int idx = tid + 256 * p, row = idx >> 4, slot = idx & 15;
+            *reinterpret_cast<u32x4*>(base + row * 256 + ((slot ^ (row & 15)) << 4)) = st[p];
+        }
+        if (tid < BM) *reinterpret_cast<u32x4*>(base + kCodeBuf + tid * 16) = sst;
     };
     u32x4 wr[4][TNW];
     auto w_issue = [&](auto slot_c, int chunk) {
@@ -1027,18 +1033,17 @@ __global__ __launch_bounds__(256) void gemm_native(const uint8_t* __restrict__ A
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // chunk at position T (0..3) of its 512-K group, activations in LDS buffer buf
-    auto compute = [&](auto t_c, int buf, const uint32_t (&wsc)[TNW]) {
+    // chunk T (0..3) of the group in LDS buffer `base`
+    auto compute = [&](auto t_c, const uint8_t* base, const uint32_t (&wsc)[TNW]) {
         constexpr int T = decltype(t_c)::value;
-        const uint8_t* base = lds + buf * kBuf;
         i32x8 a[MBW];
         int asc[MBW];
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) {
             const int row = wm * MBW * 16 + mb * 16 + r;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(base + row * 64 + j * 16);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(base + row * 256 + (((4 * T + j) ^ (row & 15)) << 4));
             a[mb] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            asc[mb] = (int)(*reinterpret_cast<const uint32_t*>(base + kCodeBuf + row * 4) >> (8 * j));
+            asc[mb] = (int)(*reinterpret_cast<const uint32_t*>(base + kCodeBuf + row * 16 + T * 4) >> (8 * j));
         }
 #pragma unroll
         for (int tt = 0; tt < TNW; ++tt) {
@@ -1051,31 +1056,33 @@ __global__ __launch_bounds__(256) void gemm_native(const uint8_t* __restrict__ A
         }
     };
     uint32_t sa[TNW], sb[TNW];
-    auto group = [&](int q, const uint32_t (&cur)[TNW], uint32_t (&nxt)[TNW]) {
+    auto group = [&](int q, int buf, const uint32_t (&cur)[TNW], uint32_t (&nxt)[TNW]) {
         const int base = 4 * q;
         const int nq = min(q + 1, q1 - 1);
+        const uint8_t* lb = lds + buf * kBuf;
 #pragma unroll
         for (int tt = 0; tt < TNW; ++tt)
             nxt[tt] = __builtin_amdgcn_raw_buffer_load_b32(rs[tt], lane * 4, nq * 256, kLoadStream);
+        a_issue(q + 1);
         auto step = [&](auto t_c) {
             constexpr int T = decltype(t_c)::value;
-            a_issue(base + T + 1);
             w_issue(std::integral_constant<int, (T + 3) % 4>{}, base + T + 3);
             __builtin_amdgcn_sched_barrier(0);
-            compute(t_c, T % 2, cur);
+            compute(t_c, lb, cur);
             __builtin_amdgcn_sched_barrier(0);
-            a_store((T + 1) % 2);
-            lds_barrier();
         };
         step(std::integral_constant<int, 0>{});
         step(std::integral_constant<int, 1>{});
         step(std::integral_constant<int, 2>{});
         step(std::integral_constant<int, 3>{});
+        a_store(1 - buf);
+        lds_barrier();
     };
 
+    const int c0 = 4 * q0;
 #pragma unroll
     for (int tt = 0; tt < TNW; ++tt) sa[tt] = __builtin_amdgcn_raw_buffer_load_b32(rs[tt], lane * 4, q0 * 256, kLoadStream);
-    a_issue(c0);
+    a_issue(q0);
     w_issue(std::integral_constant<int, 0>{}, c0);
     w_issue(std::integral_constant<int, 1>{}, c0 + 1);
     w_issue(std::integral_constant<int, 2>{}, c0 + 2);
@@ -1083,10 +1090,10 @@ __global__ __launch_bounds__(256) void gemm_native(const uint8_t* __restrict__ A
     lds_barrier();
     int q = q0;
     for (; q + 1 < q1; q += 2) {
-        group(q, sa, sb);
-        group(q + 1, sb, sa);
+        group(q, 0, sa, sb);
+        group(q + 1, 1, sb, sa);
     }
-    if (q < q1) group(q, sa, sb);
+    if (q < q1) group(q, 0, sa, sb);
 
 #pragma unroll
     for (int tt = 0; tt < TNW; ++tt)

@@ -28,6 +28,10 @@ Printed as the last stdout line, one JSON object:
   quantize     the offline quantizer (fp4_quantize) on the gate/up weight
                (57344 x 8192 BF16): GB/s of BF16 read + codes and scales
                written, both formats
+  native       (with --native) the native FP4 path (fp4_gemm_native: activations quantized
+               to MXFP4, FP4 x FP4 matrix cores, MXFP4 weights) on the same
+               four layer shapes at m = 256 (TFLOP/s against the 10.1
+               PFLOP/s dense FP4 peak) and m = 16 (GB/s)
   moe          the grouped MoE GEMM (fp4_moe_gemm): 128 experts, top-4,
                fused gate/up N = 5760, K = 2880, MXFP4, 16 and 256 tokens;
                algorithmic bytes = the routed-to experts' packed weights +
@@ -85,6 +89,7 @@ def parse():
     ap.add_argument("--no-fp16", action="store_true", help="skip the FP16-activation decode and prefill lines")
     ap.add_argument("--no-moe", action="store_true", help="skip the grouped MoE GEMM lines")
     ap.add_argument("--no-quantize", action="store_true", help="skip the quantizer line")
+    ap.add_argument("--native", action="store_true", help="also time the native FP4 path (opt-in)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (known bytes for HBM counter scaling)")
     return ap.parse_args()
@@ -232,6 +237,62 @@ def quantize_lines(args, F, torch, dev):
                                                  "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
     del Ws
     torch.cuda.empty_cache()
+    return out
+
+
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix-core peak
+
+
+def native_lines(args, F, torch, dev):
+    """fp4_gemm_native on the four Llama-3-70B layer shapes with MXFP4 weights
+    made as random packed bytes on the device (E8M0 bytes 121 .. 129; the
+    timing does not depend on the values, the GPU tests cover these shapes
+    with seeded inputs), rotating copies of >= 1 GiB per layer; activations
+    N(0, 1) in BF16, quantized inside every call."""
+    shapes = (("qkv", 10240, 8192), ("o", 8192, 8192), ("gate_up", 57344, 8192), ("down", 8192, 28672))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    lib = F.lib()
+    stream = F._c_vp(torch.cuda.current_stream().cuda_stream)
+    out = {"weights": "mxfp4 (native layout)", "activations": "bf16, quantized to mxfp4 per call",
+           "peak_TFLOP/s": MFMA_FP4_PEAK_TFLOPS, "layers": {}}
+    tot = {16: [0.0, 0.0], 256: [0.0, 0.0]}
+    for name, N, K in shapes:
+        nw, ns = F.repack_size(N, K, 1)
+        R = max(1, math.ceil(ROTATE_BYTES / (nw + ns)))
+        copies = [(torch.randint(0, 256, (nw,), dtype=torch.uint8, device=dev, generator=gen),
+                   torch.randint(121, 130, (ns,), dtype=torch.uint8, device=dev, generator=gen)) for _ in range(R)]
+        rec = {}
+        for m in (16, 256):
+            a = torch.randn((m, K), device=dev, generator=gen).to(torch.bfloat16)
+            c = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+            wsb = F.native_workspace_size(m, N, K)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            argv = [(F._dev_ptr(a), F._dev_ptr(wq), F._dev_ptr(sq), F._dev_ptr(c), m, N, K, 1.0, F._dev_ptr(ws), wsb,
+                     stream) for wq, sq in copies]
+
+            def call(s_, argv=argv):
+                st = lib.fp4_gemm_native(*argv[s_ % len(argv)])
+                if st:
+                    F._check(st, "fp4_gemm_native")
+            for s_ in range(3):
+                call(s_)
+            torch.cuda.synchronize()
+            us = timed(call, args.prefill_launches)
+            fl = 2.0 * m * N * K
+            b = algorithmic_bytes(m, N, K, 32)
+            rec[f"m{m}"] = {"us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
+                            "frac_fp4_mfma": round(fl / us / 1e6 / MFMA_FP4_PEAK_TFLOPS, 4),
+                            "GB/s": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+            tot[m][0] += fl if m == 256 else b
+            tot[m][1] += us
+        out["layers"][name] = rec
+        del copies
+        torch.cuda.empty_cache()
+    out["prefill_TFLOP/s"] = round(tot[256][0] / tot[256][1] / 1e6, 1)
+    out["prefill_frac_fp4_mfma"] = round(tot[256][0] / tot[256][1] / 1e6 / MFMA_FP4_PEAK_TFLOPS, 4)
+    out["decode_GB/s"] = round(tot[16][0] / tot[16][1] / 1e3, 1)
+    out["decode_frac_hbm"] = round(tot[16][0] / tot[16][1] / 1e3 / HBM_PEAK_GBS, 4)
     return out
 
 
@@ -413,6 +474,11 @@ def main():
         log(f"quantize 57344x8192: nvfp4 {quant['nvfp4']['us']} us ({quant['nvfp4']['GB/s']} GB/s), "
             f"mxfp4 {quant['mxfp4']['us']} us ({quant['mxfp4']['GB/s']} GB/s)")
 
+    native = None
+    if args.native:
+        native = native_lines(args, F, torch, dev)
+        log(f"native fp4: prefill m=256 {native['prefill_TFLOP/s']} TFLOP/s, decode m=16 {native['decode_GB/s']} GB/s")
+
     moe = None
     if not args.no_moe:
         moe = moe_lines(args, F, torch, synth, dev)
@@ -446,6 +512,7 @@ def main():
         "layers": per_layer,
         "prefill": prefill,
         "fp16": fp16,
+        "native": native,
         "moe": moe,
         "quantize": quant,
         "cpu_baseline": cpu,

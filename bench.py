@@ -88,6 +88,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true", help="skip the FP16-activation decode and prefill lines")
     ap.add_argument("--no-moe", action="store_true", help="skip the grouped MoE GEMM lines")
+    ap.add_argument("--no-blas", action="store_true", help="skip the BF16 hipBLASLt comparison")
     ap.add_argument("--no-quantize", action="store_true", help="skip the quantizer line")
     ap.add_argument("--native", action="store_true", help="also time the native FP4 path (opt-in)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -296,6 +297,45 @@ def native_lines(args, F, torch, dev):
     return out
 
 
+def blas_lines(args, torch, layers, per_layer, prefill, dev):
+    """Context for the Petit blog's own comparison ("Detailed performance
+    analysis": the FP4 kernel against the vendor BF16 GEMM at m = 16 and 256):
+    torch.matmul with BF16 weights of the same shapes (hipBLASLt on ROCm) on
+    this GPU, same rotation of weight copies, and the speed-up of fp4_gemm."""
+    gen = torch.Generator(device=dev).manual_seed(3)
+    out = {"library": "torch.matmul bf16 x bf16 (hipBLASLt)", "layers": {}}
+    for l in layers:
+        R = max(2, math.ceil(ROTATE_BYTES / (l.N * l.K * 2)))
+        W = [torch.randn((l.N, l.K), device=dev, generator=gen).to(torch.bfloat16) for _ in range(R)]
+        row = {}
+        for mm in (16, 256):
+            if mm == 256 and prefill is None:
+                continue
+            a = torch.randn((mm, l.K), device=dev, generator=gen).to(torch.bfloat16)
+            for s in range(5):
+                torch.matmul(a, W[s % R].t())
+            n = 30
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for s in range(n):
+                torch.matmul(a, W[s % R].t())
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / n * 1e3
+            ours = per_layer[l.name]["us"] if mm == 16 else prefill["layers"][l.name]["us"]
+            row[f"m{mm}"] = {"us": round(us, 2), "TFLOP/s": round(2.0 * mm * l.N * l.K / us / 1e6, 1),
+                             "fp4_speedup": round(us / ours, 3)}
+        out["layers"][l.name] = row
+        del W
+        torch.cuda.empty_cache()
+    for mm in (16, 256):
+        r = [v[f"m{mm}"]["fp4_speedup"] for v in out["layers"].values() if f"m{mm}" in v]
+        if r:
+            out[f"mean_speedup_m{mm}"] = round(sum(r) / len(r), 3)
+            out[f"max_speedup_m{mm}"] = round(max(r), 3)
+    return out
+
+
 def moe_lines(args, F, torch, synth, dev):
     """Grouped MoE GEMM at 16 and 256 tokens.  The expert weights are random
     packed bytes made on the device (the packed layout is a permutation of
@@ -462,6 +502,12 @@ def main():
                    "note": "weights of the decode layers; A drawn N(0,1) in BF16 with its own seed"}
         log(f"prefill m=256: {prefill['TFLOP/s']} TFLOP/s")
 
+    blas = None
+    if not args.no_blas:
+        blas = blas_lines(args, torch, layers, per_layer, prefill, dev)
+        log("hipBLASLt bf16: fp4 speed-up m=16 mean " + str(blas.get("mean_speedup_m16")) + ", m=256 mean "
+            + str(blas.get("mean_speedup_m256")))
+
     fp16 = None
     if not args.no_fp16:
         fp16 = fp16_lines(args, F, torch, layers, A, WS, dev, m)
@@ -511,6 +557,7 @@ def main():
                      "traffic": measured_traffic()},
         "layers": per_layer,
         "prefill": prefill,
+        "vs_hipblaslt_bf16": blas,
         "fp16": fp16,
         "native": native,
         "moe": moe,

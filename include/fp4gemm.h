@@ -105,12 +105,15 @@ int fp4_unpack(const uint8_t* wq, const uint8_t* sq, int64_t N, int64_t K, int f
                uint8_t* codes, uint8_t* scales);
 
 /* Workspace bytes fp4_gemm needs for this problem (a pure function of its
- * arguments; no device is queried).  For m <= 64 the library may split K over
- * S workgroups (split-K, the Petit blog's section "Detailed performance
+ * arguments; no device is queried).  The library may split K over S
+ * workgroups (split-K, the Petit blog's section "Detailed performance
  * analysis" motivates it for the skinny decode case): each writes FP32
- * partial sums of its K range and a second kernel adds them in a fixed order,
- * so the size is S * m * N * 4 bytes, or 0 when no split is chosen.  The
- * contents need no initialization and are not preserved between calls. */
+ * partial sums of its K range, which are added in a fixed order s = 0, 1, ...
+ * For m <= 64 the last workgroup of each output group adds them (it finds out
+ * through an 8-byte arrival word per group, after the partials); for m > 64 a
+ * second kernel does.  The size is about S * m * N * 4 bytes, or 0 when no
+ * split is chosen.  The contents need no initialization (the arrival words
+ * carry a tag unique to each launch) and are not preserved between calls. */
 int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int format, size_t* bytes);
 
 /* Y = A . dequant(W)^T on `stream` (a hipStream_t; NULL = default stream).
@@ -128,7 +131,7 @@ int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int format, size_t*
  * are queued; faults surface at the caller's next synchronization.
  * Accumulation is FP32; the output is rounded to BF16 to nearest even.
  * Results are deterministic: the same inputs give the same bits on every
- * call (fixed summation order, no atomics). */
+ * call (fixed summation order; the only atomics count split-K arrivals). */
 int fp4_gemm(const void* A, const void* wq, const void* sq, void* C,
              int64_t m, int64_t N, int64_t K, int format,
              void* workspace, size_t workspace_bytes, void* stream);

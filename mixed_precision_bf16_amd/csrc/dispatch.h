@@ -49,11 +49,15 @@ struct MoeArgs {
     X(1, 8, 8, 2) X(1, 8, 8, 1)
 
 // Launch one GEMM kernel on stream s (P: FP32 partials of a K split, else
-// null).  False when the shape is not compiled.
+// null).  False when the shape is not compiled.  The decode kernel finishes
+// its K split itself (arrival words after the partials, `tag` unique to the
+// launch); the prefill kernel leaves the partials to reduce_partials.
 bool launch_decode_bf16(int fmt, int MB, const DecodeShape& d, const void* A, const void* wq, const void* sq,
-                        void* C, float* P, int M, int N, int K, int KB, int SB, int NT, float alpha, hipStream_t s);
+                        void* C, float* P, int M, int N, int K, int KB, int SB, int NT, float alpha, uint32_t tag,
+                        hipStream_t s);
 bool launch_decode_f16(int fmt, int MB, const DecodeShape& d, const void* A, const void* wq, const void* sq, void* C,
-                       float* P, int M, int N, int K, int KB, int SB, int NT, float alpha, hipStream_t s);
+                       float* P, int M, int N, int K, int KB, int SB, int NT, float alpha, uint32_t tag,
+                       hipStream_t s);
 bool launch_prefill_bf16(int fmt, const PrefillShape& t, const void* A, const void* wq, const void* sq, void* C,
                          float* P, int M, int N, int K, int KB, int SB, int NT, float alpha, hipStream_t s);
 bool launch_prefill_f16(int fmt, const PrefillShape& t, const void* A, const void* wq, const void* sq, void* C,

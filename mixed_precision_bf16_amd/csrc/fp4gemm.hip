@@ -40,14 +40,12 @@ static int64_t a_row_block(int64_t M) {
     return 128;  // prefill m-block
 }
 
+// Tuning override, read on every call so that a tuning run can change it.
 static DecodeShape decode_override() {
-    static const DecodeShape ov = [] {
-        DecodeShape d{0, 0, 0, 0};
-        const char* e = getenv("FP4GEMM_DECODE");
-        if (e) sscanf(e, "%d,%d,%d,%d", &d.tn, &d.nwn, &d.nwk, &d.s);
-        return d;
-    }();
-    return ov;
+    DecodeShape d{0, 0, 0, 0};
+    const char* e = getenv("FP4GEMM_DECODE");
+    if (e && *e) sscanf(e, "%d,%d,%d,%d", &d.tn, &d.nwn, &d.nwk, &d.s);
+    return d;
 }
 
 static bool decode_compiled(int MB, const DecodeShape& d);
@@ -65,8 +63,9 @@ constexpr int kCUs = 256;  // compute units of an MI355X / MI350X (gfx950)
 // (rows past m read nothing); every workgroup pays ~1.5 us before its first
 // block arrives; a CU needs ~24 KiB of code blocks in flight (three chunks
 // ahead per wave) to cover the memory latency; a K split over S workgroups
-// adds the partial sums' round trip and one reduce launch (~5 us with its
-// launch gap).
+// adds the partial sums' round trip, the arrival count and the last
+// workgroup's pass over the partials (~5 us in all, fit to the measured
+// shapes).
 static double decode_cost(int fmt, int MB, int64_t M, int64_t N, int NT, int SB, const DecodeShape& d) {
     const int g = d.tn * d.nwn;
     const int groups = (NT + g - 1) / g;
@@ -83,9 +82,9 @@ static double decode_cost(int fmt, int MB, int64_t M, int64_t N, int NT, int SB,
     if (inflight < 24.0 * 1024.0) t *= 24.0 * 1024.0 / inflight;
     if (d.s > 1) t += 5e-6 + 2.0 * d.s * (double)M * (double)N * 4.0 / 2e12;
     // Ties between shapes that move the same bytes: fewer tiles per wave
-    // (shorter dependency chains) and fewer K groups (no LDS reduction) measure
-    // slightly faster.
-    return t * (1.0 + 0.03 * (d.tn - 1)) * (1.0 + 0.02 * (d.nwk - 1));
+    // (shorter dependency chains) and more K groups (the waves of a group
+    // share one activation stream) measure slightly faster.
+    return t * (1.0 + 0.03 * (d.tn - 1)) * (1.0 - 0.01 * (d.nwk - 1));
 }
 
 // Shape for m <= 16 * MB: the compiled shape and K split with the least
@@ -94,6 +93,7 @@ static DecodeShape pick_decode(int fmt, int MB, int64_t M, int64_t N, int NT, in
     DecodeShape d = decode_override();
     if (d.tn > 0 && decode_compiled(MB, d)) {
         d.s = d.s < 1 ? 1 : (d.s > SB ? SB : d.s);
+        if (M * N >= (int64_t(1) << 29)) d.s = 1;
         return d;
     }
     int count = 0;
@@ -103,7 +103,7 @@ static DecodeShape pick_decode(int fmt, int MB, int64_t M, int64_t N, int NT, in
     for (int i = 0; i < count; ++i) {
         if (c[i].mb != MB) continue;
         for (int S : {1, 2, 4, 8, 16}) {
-            if (S > SB) break;
+            if (S > SB || (S > 1 && M * N >= (int64_t(1) << 29))) break;  // partial planes use 32-bit offsets
             const DecodeShape cand{c[i].tn, c[i].nwn, c[i].nwk, S};
             if (c[i].nwk > (SB + S - 1) / S) continue;  // every K group gets a block
             const double t = decode_cost(fmt, MB, M, N, NT, SB, cand);
@@ -116,8 +116,21 @@ static DecodeShape pick_decode(int fmt, int MB, int64_t M, int64_t N, int NT, in
     return best;
 }
 
-static size_t decode_workspace_bytes(const DecodeShape& d, int64_t M, int64_t N) {
-    return d.s > 1 ? (size_t)d.s * (size_t)M * (size_t)N * sizeof(float) : 0;
+// K split: S partial planes of M x N FP32, then one 8-byte arrival word per
+// workgroup group (split_counter_floats in kernels.h).
+static size_t decode_workspace_bytes(const DecodeShape& d, int64_t M, int64_t N, int NT) {
+    if (d.s <= 1) return 0;
+    const int groups = (NT + d.tn * d.nwn - 1) / (d.tn * d.nwn);
+    return split_counter_floats(d.s, int(M), int(N)) * sizeof(float) + (size_t)groups * 8;
+}
+
+// Launch tags of the split-K arrival words: unique per launch (never 0).
+static std::atomic<uint32_t> g_split_tag{0};
+static uint32_t next_split_tag() {
+    uint32_t t;
+    do t = g_split_tag.fetch_add(1, std::memory_order_relaxed) + 1;
+    while (t == 0);
+    return t;
 }
 
 static const DecodeCand* decode_shapes(int* count) {
@@ -146,13 +159,10 @@ static void launch_reduce(int act, const float* P, void* C, int64_t total, int S
 }
 
 static PrefillShape prefill_override() {
-    static const PrefillShape ov = [] {
-        PrefillShape t{0, 0, 0, 0, 1};
-        const char* e = getenv("FP4GEMM_PREFILL");
-        if (e) sscanf(e, "%d,%d,%d,%d,%d", &t.wm, &t.wn, &t.mbw, &t.tnw, &t.s);
-        return t;
-    }();
-    return ov;
+    PrefillShape t{0, 0, 0, 0, 1};
+    const char* e = getenv("FP4GEMM_PREFILL");
+    if (e && *e) sscanf(e, "%d,%d,%d,%d,%d", &t.wm, &t.wn, &t.mbw, &t.tnw, &t.s);
+    return t;
 }
 
 static bool prefill_compiled(const PrefillShape& t) {
@@ -205,11 +215,10 @@ static int launch_gemm(int fmt, int act, const void* A, const void* wq, const vo
         const int MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
         const DecodeShape d = pick_decode(fmt, MB, M, N, NT, SB);
         float* P = d.s > 1 ? static_cast<float*>(ws) : nullptr;
-        const bool ok = act == 0 ? launch_decode_bf16(fmt, MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, s)
-                                 : launch_decode_f16(fmt, MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, s);
-        if (!ok) return FP4_ERR_SHAPE;
-        if (P) launch_reduce(act, P, C, (int64_t)M * N, d.s, alpha, s);
-        return FP4_OK;
+        const uint32_t tag = P ? next_split_tag() : 0u;
+        const bool ok = act == 0 ? launch_decode_bf16(fmt, MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, tag, s)
+                                 : launch_decode_f16(fmt, MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, tag, s);
+        return ok ? FP4_OK : FP4_ERR_SHAPE;
     }
     const PrefillShape t = pick_prefill(fmt, M, N, NT, SB);
     float* P = t.s > 1 ? static_cast<float*>(ws) : nullptr;
@@ -229,7 +238,7 @@ static size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
         return t.s > 1 ? (size_t)t.s * (size_t)M * (size_t)N * sizeof(float) : 0;
     }
     const int MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    return decode_workspace_bytes(pick_decode(fmt, MB, M, N, NT, SB), M, N);
+    return decode_workspace_bytes(pick_decode(fmt, MB, M, N, NT, SB), M, N, NT);
 }
 
 // alpha: finite, |alpha| in [2^-100, 2^100] or exactly 1 (checked by the entries).

@@ -63,6 +63,10 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // weight codes and scales): the nontemporal hint.
 constexpr int kLoadStream = 2;
 constexpr int kXcdCount = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+// Cache-policy operand sc1 (device scope): the access is coherent across the
+// XCDs' separate L2 caches (stores write through, loads do not hit a line
+// another XCD may have changed).  Used for the split-K partial sums.
+constexpr int kDeviceCoherent = 16;
 
 // ------------------------------------------------------------------ dequant
 // Keep the upper 16 bits of two FP32 values (exact when both are BF16 values).
@@ -203,6 +207,125 @@ __device__ __forceinline__ u32x4 load_scale_block(__amdgpu_buffer_rsrc_t r, int 
     return __builtin_amdgcn_raw_buffer_load_b128(r, soff_lane, sb * scale_block_bytes<FMT>(), kLoadStream);
 }
 
+// ------------------------------------------------------------ split-K fixup
+// A K split over S workgroups without a second kernel.  Each workgroup of a
+// group writes its FP32 partial sums P[ks][m][n] with device-coherent stores,
+// waits until they are complete and counts itself in at the group's arrival
+// word; the workgroup that arrives last adds the S partials in the fixed
+// order s = 0, 1, ... (device-coherent loads), scales by alpha and writes
+// the output.  Because every access to the partials and to the arrival word
+// is device-coherent, no cache-wide write-back or invalidate is needed.
+// The arrival word is (tag << 32) | count with a tag unique to the launch:
+// a word holding any other tag (stale words of earlier launches, partial
+// sums of other shapes, uninitialized memory) counts as zero, so the
+// workspace needs no initialization.  The arrival words follow the partials
+// at a 256-byte aligned offset (in floats):
+__host__ __device__ inline size_t split_counter_floats(int S, int M, int N) {
+    return ((size_t)S * (size_t)M * (size_t)N + 63) / 64 * 64;
+}
+
+// Partial plane ks of an S-way split (M x N FP32, M * N < 2^29).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t split_plane(const float* P, int ks, int M, int N) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(P) + (size_t)ks * M * N, 0, M * N * 4, kBufWord3);
+}
+
+// Store the FP32 partials of one 16x16 output fragment (lane: row m, columns
+// n0 .. n0 + 3) into plane `pl`; columns at or past N are dropped.
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t pl, const f32x4& v, int m, int n0, int N) {
+    const uint32_t off = (uint32_t)(m * N + n0) * 4u;
+    if ((N & 3) == 0 && n0 + 3 < N) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), pl, off, 0, kDeviceCoherent);
+    } else {
+        for (int e = 0; e < 4; ++e)
+            if (n0 + e < N) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), pl, off + 4 * e, 0,
+                                                                  kDeviceCoherent);
+    }
+}
+
+// Count one arrival at word w; true for the S-th arrival of this launch.
+__device__ __forceinline__ bool split_arrive(unsigned long long* w, uint32_t tag, int S) {
+    unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {  // each failed exchange is another workgroup's arrival: at most S - 1 retries
+        const uint32_t cnt = (uint32_t)(old >> 32) == tag ? (uint32_t)old : 0u;
+        const unsigned long long nw = ((unsigned long long)tag << 32) | (unsigned long long)(cnt + 1);
+        if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return cnt + 1 == (uint32_t)S;
+    }
+}
+
+// Y[m][n] = alpha * sum_s P[s][m][n] over the rows [m_begin, m_end) and
+// columns [n_begin, n_end), in the order s = 0, 1, ... (SS: S known at
+// compile time, else 0).
+template <int ACT, int kThreads, int SS>
+__device__ __forceinline__ void split_sum(const float* P, uint16_t* __restrict__ C, int M, int N, int S, int m_begin,
+                                          int m_end, int n_begin, int n_end, float alpha) {
+    const int quads = (n_end - n_begin + 3) >> 2;
+    const int total = (m_end - m_begin) * quads;
+    for (int e = threadIdx.x; e < total; e += kThreads) {
+        const int m = m_begin + e / quads, n = n_begin + 4 * (e % quads);
+        const uint32_t off = (uint32_t)(m * N + n) * 4u;
+        if ((N & 3) == 0 && n + 3 < N) {
+            f32x4 v;
+            if constexpr (SS > 0) {
+                u32x4 p[SS];
+#pragma unroll
+                for (int s = 0; s < SS; ++s)
+                    p[s] = __builtin_amdgcn_raw_buffer_load_b128(split_plane(P, s, M, N), off, 0, kDeviceCoherent);
+                v = __builtin_bit_cast(f32x4, p[0]);
+#pragma unroll
+                for (int s = 1; s < SS; ++s) v += __builtin_bit_cast(f32x4, p[s]);
+            } else {
+                v = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(split_plane(P, 0, M, N), off, 0, kDeviceCoherent));
+                for (int s = 1; s < S; ++s)
+                    v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(split_plane(P, s, M, N), off,
+                                                                                         0, kDeviceCoherent));
+            }
+            v *= alpha;
+            u32x2 o = {pack_out<ACT>(v.x, v.y), pack_out<ACT>(v.z, v.w)};
+            *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = o;
+        } else {
+            for (int x = 0; x < 4 && n + x < n_end; ++x) {
+                float v = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(split_plane(P, 0, M, N), off + 4 * x, 0, kDeviceCoherent));
+                for (int s = 1; s < S; ++s)
+                    v += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(split_plane(P, s, M, N), off + 4 * x,
+                                                                              0, kDeviceCoherent));
+                v *= alpha;
+                C[(size_t)m * N + n + x] = (uint16_t)(pack_out<ACT>(v, 0.f) & 0xFFFF);
+            }
+        }
+    }
+}
+
+// Called by every thread of the workgroup after its partial stores (no
+// thread may have exited).  Returns in all threads; the last arriving
+// workgroup of the group first writes Y[m][n] = alpha * sum_s P[s][m][n]
+// for m in [m_begin, m_end), n in [n_begin, n_end).
+template <int ACT, int kThreads>
+__device__ __forceinline__ void split_finish(const float* P, uint16_t* __restrict__ C, int M, int N, int S, int grp,
+                                             int m_begin, int m_end, int n_begin, int n_end, float alpha,
+                                             uint32_t tag) {
+    __shared__ int last;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long* words =
+            reinterpret_cast<unsigned long long*>(const_cast<float*>(P) + split_counter_floats(S, M, N));
+        last = split_arrive(words + grp, tag, S);
+    }
+    __syncthreads();
+    if (!last) return;
+    asm volatile("" ::: "memory");
+    switch (S) {  // a compile-time S keeps all S loads of an output in flight at once
+        case 2: split_sum<ACT, kThreads, 2>(P, C, M, N, S, m_begin, m_end, n_begin, n_end, alpha); break;
+        case 4: split_sum<ACT, kThreads, 4>(P, C, M, N, S, m_begin, m_end, n_begin, n_end, alpha); break;
+        case 8: split_sum<ACT, kThreads, 8>(P, C, M, N, S, m_begin, m_end, n_begin, n_end, alpha); break;
+        default: split_sum<ACT, kThreads, 0>(P, C, M, N, S, m_begin, m_end, n_begin, n_end, alpha); break;
+    }
+}
+
 // ------------------------------------------------------------ MoE routing
 // Grouped mixture-of-experts GEMM (the petit-kernel page, "Features": fused
 // MoE kernels for BF16 x MXFP4): expert e owns the packed weights at
@@ -281,7 +404,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
                                                              const uint8_t* __restrict__ sq,
                                                              uint16_t* __restrict__ C, float* __restrict__ P, int M,
                                                              int N, int K, int KB, int SB, int NT, int S,
-                                                             float alpha, MoeArgs moe = MoeArgs{}) {
+                                                             float alpha, uint32_t tag, MoeArgs moe = MoeArgs{}) {
     typedef u32x4 SW;
     constexpr int kRows = 16 * MB;  // activation rows; one 1 KiB load per row per block
     // Activation load instructions per wave per block.  When NWN does not
@@ -366,7 +489,11 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 wr[4][TN];
+    // Code ring: kSlots slots, chunks issued kAhead = kSlots - 1 steps ahead
+    // (a ring of 8 measured no faster on MI355X).
+    constexpr int kSlots = 4;
+    constexpr int kAhead = kSlots - 1;
+    u32x4 wr[kSlots][TN];
     u32x4 ar[QB];
     SW sa[TN], sbs[TN];
     // activations of block sbx into registers
@@ -387,11 +514,14 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
     // Code blocks wholly past K (the zero padding of K to 512) are not
     // fetched: an out-of-range offset makes the load return zeros without a
     // memory access.
+    // Prefetches past the group's last chunk are never multiplied: they too
+    // read nothing.
     const int kb_valid = (K + kChunkK - 1) / kChunkK;
     auto w_issue = [&](auto slot_c, int chunk) {
         constexpr int SL = decltype(slot_c)::value;
+        const bool live = chunk <= cmax && chunk < kb_valid;
         chunk = min(chunk, cmax);
-        const uint32_t voff = (uint32_t)lane * 16u + (chunk < kb_valid ? 0u : kOutOfRange);
+        const uint32_t voff = (uint32_t)lane * 16u + (live ? 0u : kOutOfRange);
 #pragma unroll
         for (int tt = 0; tt < TN; ++tt)
             wr[SL][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], voff, chunk * 1024, kLoadStream);
@@ -401,9 +531,10 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
-    // multiply chunk T of the block in LDS buffer buf with code slot T
-    auto compute = [&](auto slot_c, const uint8_t* blk_base, const SW (&sc)[TN]) {
-        constexpr int T = decltype(slot_c)::value;
+    // multiply chunk T of the block in LDS buffer buf with code slot SL
+    auto compute = [&](auto t_c, auto slot_c, const uint8_t* blk_base, const SW (&sc)[TN]) {
+        constexpr int T = decltype(t_c)::value;
+        constexpr int SL = decltype(slot_c)::value;
         const uint8_t* base = blk_base + T * kBuf;
         auto step = [&](auto ii) {
             constexpr int I = decltype(ii)::value;
@@ -414,7 +545,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
                 a[mb] = *reinterpret_cast<const u32x4*>(base + ((I * MB + mb) * 64 + slot) * 16);
 #pragma unroll
             for (int tt = 0; tt < TN; ++tt) {
-                const u32x4 wf = dequant_step<FMT, T, I, ACT>(wr[T][tt], sc[tt]);
+                const u32x4 wf = dequant_step<FMT, T, I, ACT>(wr[SL][tt], sc[tt]);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) acc[tt][mb] = mfma<ACT>(wf, a[mb], acc[tt][mb]);
             }
@@ -424,11 +555,14 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
         step(std::integral_constant<int, 2>{});
         step(std::integral_constant<int, 3>{});
     };
-    auto pstep = [&](auto slot_c, int base, bool valid, const uint8_t* blk_base, const SW (&cur)[TN]) {
-        constexpr int T = decltype(slot_c)::value;
-        w_issue(std::integral_constant<int, (T + 3) % 4>{}, base + T + 3);
+    // chunk T of a block of parity PAR: the ring slot of the chunk c0 + 4 blk
+    // + T is (4 PAR + T) % kSlots (blocks alternate parity from blk = 0)
+    auto pstep = [&](auto par_c, auto t_c, int base, bool valid, const uint8_t* blk_base, const SW (&cur)[TN]) {
+        constexpr int PAR = decltype(par_c)::value;
+        constexpr int T = decltype(t_c)::value;
+        w_issue(std::integral_constant<int, (4 * PAR + T + kAhead) % kSlots>{}, base + T + kAhead);
         __builtin_amdgcn_sched_barrier(0);
-        if (valid) compute(slot_c, blk_base, cur);
+        if (valid) compute(t_c, std::integral_constant<int, (4 * PAR + T) % kSlots>{}, blk_base, cur);
         __builtin_amdgcn_sched_barrier(0);
     };
     // one 512-K block (x = blk, LDS buffer PAR = blk % 2): chunks 4 (sb0 + blk)
@@ -444,10 +578,10 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
 #pragma unroll
         for (int tt = 0; tt < TN; ++tt) nxt[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
         const uint8_t* blk_base = ring + PAR * kBlk;
-        pstep(std::integral_constant<int, 0>{}, base, valid, blk_base, cur);
-        pstep(std::integral_constant<int, 1>{}, base, valid, blk_base, cur);
-        pstep(std::integral_constant<int, 2>{}, base, valid, blk_base, cur);
-        pstep(std::integral_constant<int, 3>{}, base, valid, blk_base, cur);
+        pstep(par_c, std::integral_constant<int, 0>{}, base, valid, blk_base, cur);
+        pstep(par_c, std::integral_constant<int, 1>{}, base, valid, blk_base, cur);
+        pstep(par_c, std::integral_constant<int, 2>{}, base, valid, blk_base, cur);
+        pstep(par_c, std::integral_constant<int, 3>{}, base, valid, blk_base, cur);
         a_store(1 - PAR);
     };
 
@@ -476,15 +610,17 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
                     red[((((wk - 1) * NWN + wn) * TN + tt) * MB + mb) * kLanes + lane] = acc[tt][mb];
         }
         __syncthreads();
-        if (wk != 0) return;
-        for (int g = 1; g < NWK; ++g)
+        if (wk == 0)
+            for (int g = 1; g < NWK; ++g)
 #pragma unroll
-            for (int tt = 0; tt < TN; ++tt)
+                for (int tt = 0; tt < TN; ++tt)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[tt][mb] += red[((((g - 1) * NWN + wn) * TN + tt) * MB + mb) * kLanes + lane];
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[tt][mb] += red[((((g - 1) * NWN + wn) * TN + tt) * MB + mb) * kLanes + lane];
     }
+    // the waves of K group 0 hold the workgroup's sums
     if constexpr (MOE) {
+        if (wk != 0) return;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int m = mb * 16 + r;
@@ -498,23 +634,27 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
         }
         return;
     }
+    if (P == nullptr) {
+        if (wk != 0) return;
 #pragma unroll
-    for (int tt = 0; tt < TN; ++tt)
+        for (int tt = 0; tt < TN; ++tt)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int m = mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
-            if (P == nullptr) {
-                store_frag<ACT>(C, acc[tt][mb] * alpha, m, n0, M, N);
-            } else if (m < M) {
-                float* dst = P + ((size_t)ks * M + m) * N + n0;
-                if ((N & 3) == 0 && n0 + 3 < N) {
-                    *reinterpret_cast<f32x4*>(dst) = acc[tt][mb];
-                } else {
-                    for (int e = 0; e < 4; ++e)
-                        if (n0 + e < N) dst[e] = acc[tt][mb][e];
-                }
-            }
-        }
+            for (int mb = 0; mb < MB; ++mb)
+                store_frag<ACT>(C, acc[tt][mb] * alpha, mb * 16 + r, (tile0 + tt) * kTileN + 4 * j, M, N);
+        return;
+    }
+    // K split: partials, then the group's last workgroup writes the output
+    if (wk == 0) {
+        const __amdgpu_buffer_rsrc_t pl = split_plane(P, ks, M, N);
+#pragma unroll
+        for (int tt = 0; tt < TN; ++tt)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                if (mb * 16 + r < M) store_partial(pl, acc[tt][mb], mb * 16 + r, (tile0 + tt) * kTileN + 4 * j, N);
+    }
+    const int n_begin = grp * (TN * NWN) * kTileN;
+    split_finish<ACT, 64 * NWN * NWK>(P, C, M, N, S, grp, 0, M, n_begin, min(N, n_begin + TN * NWN * kTileN), alpha,
+                                      tag);
 }
 
 // Y = alpha x the sum over s of the S partial products P[s][M][N] (in order

@@ -11,7 +11,7 @@ void launch_moe_t(const void* A, const void* wq, const void* sq, void* C, const 
                   int SB, int NT, int items, hipStream_t s) {
     const int groups = (NT + TN * NWN - 1) / (TN * NWN);
     gemm_decode<FMT, 0, MB, TN, NWN, 1, true><<<dim3(groups, items), dim3(64 * NWN), 0, s>>>(
-        (const uint16_t*)A, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, nullptr, 0, N, K, KB, SB, NT, 1, 1.0f, moe);
+        (const uint16_t*)A, (const u32x4*)wq, (const uint8_t*)sq, (uint16_t*)C, nullptr, 0, N, K, KB, SB, NT, 1, 1.0f, 0u, moe);
 }
 
 template <int FMT>

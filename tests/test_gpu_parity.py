@@ -280,13 +280,15 @@ def test_repeat_runs_bit_identical(m, act):
 
 
 def test_one_workspace_reused_across_shapes_and_calls():
-    # split-K partial sums live in the workspace: stale contents from a call of
-    # another shape must not leak into the next result
+    # split-K partial sums and arrival words live in the workspace: neither
+    # uninitialized contents nor stale contents from a call of another shape
+    # may leak into the next result
     shapes = [(16, 10240, 8192, 0), (1, 1000, 8192, 0), (16, 8192, 28672, 1), (7, 8200, 8192, 0),
-              (256, 520, 2048, 0)]
+              (256, 520, 2048, 0), (64, 4000, 8192, 0), (16, 10240, 8192, 0)]
     need = max(F.workspace_size(m, N, K, f) for m, N, K, f in shapes)
     assert need > 0
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator().manual_seed(7)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=gen).to("cuda")
     for rep in range(2):
         for m, N, K, fmt in shapes:
             _say("workspace reuse", rep, m, N, K, fmt)

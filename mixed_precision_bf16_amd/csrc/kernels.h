@@ -687,20 +687,18 @@ __global__ __launch_bounds__(256) void reduce_partials(const float* __restrict__
 // TNW n-tiles), over a K range (the whole K, or 1/S of it with FP32
 // partials).  Eight waves run two per SIMD, so one wave's dequant and memory
 // instructions issue while the other's matrix instructions execute.
-// Activations go global -> registers -> LDS (two chunk buffers, XOR-swizzled
-// by row: conflict-free 16-byte writes and fragment reads; the Petit blog,
-// "Mastering the memory hierarchy"); codes go global -> registers through a
-// 4-slot ring, three chunks ahead; scales one 512-K block ahead.
-// Per 128-K chunk c (four MFMA steps i = 0..3), with the activation
-// fragments of each step read from LDS one step ahead:
+// Activations go global -> LDS by DMA (three chunk buffers in rotation,
+// XOR-swizzled by row: conflict-free fragment reads; the Petit blog,
+// "Mastering the memory hierarchy"), so they take no registers; codes go
+// global -> registers through a 4-slot ring, three chunks ahead; scales one
+// 512-K block ahead.  Per 128-K chunk c (four MFMA steps i = 0..3), with the
+// activation fragments of each step read from LDS one step ahead:
 //   issue the code blocks of chunk c+3;
 //   steps 0..2 of chunk c, each reading the fragments of the next step;
-//   barrier: every wave is done with LDS buffer c % 2, and the chunk c+1
-//     activations written one chunk earlier are visible;
-//   write the activations of chunk c+2 to buffer c % 2 and issue those of
-//     chunk c+4 (two register sets) or c+3 (one set, for the shapes whose
-//     accumulators leave no room for two) into the freed register set;
-//   step 3 of chunk c, reading step 0 of chunk c+1 from buffer (c+1) % 2.
+//   wait for this wave's DMA of chunk c+1, then barrier: every wave is done
+//     with chunk c's buffer and chunk c+1 is in LDS;
+//   DMA chunk c+3 into chunk c's buffer (two chunks of time to land);
+//   step 3 of chunk c, reading step 0 of chunk c+1.
 // So no fragment read waits on its own step's products, and the one barrier
 // per chunk sits where three steps' products are still in flight.
 template <int FMT, int ACT, int WM, int WN, int MBW, int TNW, bool KTAIL>
@@ -718,7 +716,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
     constexpr int kStage = BM * 16 / kThreads;  // 16-byte activation pieces per thread per chunk
     static_assert(kStage * kThreads == BM * 16, "whole pieces per thread");
     constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[3 * kBuf];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -750,37 +748,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
         rs[tt] = make_rsrc(sq + (size_t)t * SB * kScaleBlockBytes, (uint32_t)(SB * kScaleBlockBytes));
     }
 
-    // activation staging: piece q of this thread = (row, 16-byte column)
+    // Activations move HBM/L2 -> LDS by DMA (buffer loads that write LDS, no
+    // registers): piece q of a wave is one 1 KiB instruction, lane l writing
+    // the 16 bytes at LDS slot p = q * kThreads + 64 * wave + l of the chunk
+    // buffer (row p / 16, physical column p % 16).  The tile is XOR-swizzled
+    // by row (physical column = logical column ^ (row % 16): conflict-free
+    // fragment reads; the Petit blog, "Mastering the memory hierarchy"), so
+    // the lane fetches logical column (p % 16) ^ (row % 16) of its row.
     uint32_t aoff[kStage];
-    int lds_off[kStage];
+    int acol[kStage];
 #pragma unroll
     for (int q = 0; q < kStage; ++q) {
         const int idx = tid + kThreads * q;
-        const int row = idx >> 4, col = idx & 15;
+        const int row = idx >> 4, col = (idx & 15) ^ (row & 15);
+        acol[q] = col;
         aoff[q] = (uint32_t)((m0 + row) * K + col * 8) * 2u;
-        lds_off[q] = row * 256 + ((col ^ (row & 15)) << 4);
     }
-    // Register sets for activations in flight: two (issued two chunks before
-    // they are written to LDS) when the registers leave room (eight waves:
-    // half the pieces per thread; four waves: fewer than 32 accumulator
-    // tiles), else one.
-    constexpr int kSets = (WM * WN == 8 || MBW * TNW < 32) ? 2 : 1;
-    u32x4 st[kSets][kStage];
-    auto a_issue = [&](auto set_c, int chunk) {
-        constexpr int SET = decltype(set_c)::value % kSets;
+    // chunk -> LDS buffer at byte offset buf (three buffers in rotation).
+    // A prefetch past the range repeats the last chunk into a buffer nobody
+    // reads again.
+    auto a_dma = [&](int chunk, int buf) {
         chunk = min(chunk, clast);
 #pragma unroll
         for (int q = 0; q < kStage; ++q) {
-            const int k = chunk * kChunkK + (((tid + kThreads * q) & 15) * 8);
+            const int k = chunk * kChunkK + acol[q] * 8;
             const uint32_t off = aoff[q] + (uint32_t)(chunk * kChunkK) * 2u;
-            st[SET][q] = load_a(ra, (!KTAIL || k < K) ? off : kOutOfRange);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void*)(lds_a + buf + (q * kThreads + 64 * wave) * 16), 16,
+                (!KTAIL || k < K) ? off : kOutOfRange, 0, 0, 0);
         }
-    };
-    auto a_store = [&](auto set_c, auto buf_c) {
-        constexpr int SET = decltype(set_c)::value % kSets;
-        constexpr int BUF = decltype(buf_c)::value;
-#pragma unroll
-        for (int q = 0; q < kStage; ++q) *reinterpret_cast<u32x4*>(lds_a + BUF * kBuf + lds_off[q]) = st[SET][q];
     };
     u32x4 wr[4][TNW];
     auto w_issue = [&](auto slot_c, int chunk) {
@@ -790,21 +786,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
         for (int tt = 0; tt < TNW; ++tt)
             wr[SL][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, kLoadStream);
     };
+    // Barrier between the waves' LDS accesses.  Written without a fence: a
+    // workgroup fence would also make every wave wait for its newest LDS DMA
+    // (issued one chunk earlier), which the schedule waits for one chunk
+    // later, explicitly (kYounger below).  The waits here cover this wave's
+    // fragment reads; the memory clobbers keep LDS accesses on their side.
     auto lds_barrier = [] {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        asm volatile("" ::: "memory");
     };
     // this lane's fragments (16-byte column 4 I + j of its rows) of step I
-    // of the chunk in LDS buffer BUF
-    auto read_frags = [&](auto i_c, auto buf_c, u32x4 (&a)[MBW]) {
+    // of the chunk in the LDS buffer at byte offset buf
+    auto read_frags = [&](auto i_c, int buf, u32x4 (&a)[MBW]) {
         constexpr int I = decltype(i_c)::value;
-        constexpr int BUF = decltype(buf_c)::value;
+        const uint8_t* base = lds_a + buf + (wm * MBW * 16 + r) * 256 + (((4 * I + j) ^ r) << 4);
 #pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) {
-            const int row = wm * MBW * 16 + mb * 16 + r;
-            a[mb] = *reinterpret_cast<const u32x4*>(lds_a + BUF * kBuf + row * 256 + (((4 * I + j) ^ (row & 15)) << 4));
-        }
+        for (int mb = 0; mb < MBW; ++mb) a[mb] = *reinterpret_cast<const u32x4*>(base + mb * 16 * 256);
     };
 
     f32x4 acc[TNW][MBW];
@@ -841,56 +839,49 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    // Four-wave shapes read each step's fragments one step ahead (two
-    // fragment sets); eight-wave shapes have no registers to spare for that
-    // and rely on the other wave of their SIMD to cover the LDS latency.
-    constexpr bool kPrefetch = WM * WN == 4;
-    u32x4 fa[MBW], fb[kPrefetch ? MBW : 1];
-    // chunk c = base + T (T = c % 4; c % 2 == T % 2); fa holds step 0's
-    // fragments when prefetching
+    // Each step's fragments are read one step ahead (two fragment sets).
+    u32x4 fa[MBW], fb[MBW];
+    // LDS buffers (byte offsets): chunk c in b_cur, c+1 in b_nxt, the DMA of
+    // c+2 in flight to b_far.
+    int b_cur = 0, b_nxt = kBuf, b_far = 2 * kBuf;
+    // Vector-memory instructions certainly issued after the DMA of chunk c+1
+    // by the time chunk c waits for it: the DMA of chunk c+2.  Loads complete
+    // in issue order, so at most this many may then be outstanding.  (The code
+    // loads in between are not counted: the compiler deletes the prefetches
+    // of the last block whose results are never used.)
+    constexpr int kYounger = kStage;
+    // chunk c = base + T (T = c % 4, also its code-ring slot); fa holds step
+    // 0's fragments on entry
     auto pstep = [&](auto t_c, int base, const SW (&cur)[TNW]) {
         constexpr int T = decltype(t_c)::value;
-        using B = std::integral_constant<int, T % 2>;
         w_issue(std::integral_constant<int, (T + 3) % 4>{}, base + T + 3);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (!kPrefetch) {
-            auto one = [&](auto i_c) {
-                read_frags(i_c, B{}, fa);
-                mma(t_c, i_c, fa, cur);
-                interleave();
-                __builtin_amdgcn_sched_barrier(0);
-            };
-            one(I0{});
-            one(I1{});
-            one(I2{});
-            one(I3{});
-            lds_barrier();
-            a_store(B{}, B{});
-            a_issue(B{}, base + T + 2 + kSets);
-            __builtin_amdgcn_sched_barrier(0);
-        } else {
-            using NB = std::integral_constant<int, (T + 1) % 2>;
-            read_frags(I1{}, B{}, fb);
-            mma(t_c, I0{}, fa, cur);
-            interleave();
-            __builtin_amdgcn_sched_barrier(0);
-            read_frags(I2{}, B{}, fa);
-            mma(t_c, I1{}, fb, cur);
-            interleave();
-            __builtin_amdgcn_sched_barrier(0);
-            read_frags(I3{}, B{}, fb);
-            mma(t_c, I2{}, fa, cur);
-            interleave();
-            __builtin_amdgcn_sched_barrier(0);
-            lds_barrier();
-            a_store(B{}, B{});
-            a_issue(B{}, base + T + 2 + kSets);
-            __builtin_amdgcn_sched_barrier(0);
-            read_frags(I0{}, NB{}, fa);
-            mma(t_c, I3{}, fb, cur);
-            interleave();
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        read_frags(I1{}, b_cur, fb);
+        mma(t_c, I0{}, fa, cur);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(I2{}, b_cur, fa);
+        mma(t_c, I1{}, fb, cur);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(I3{}, b_cur, fb);
+        mma(t_c, I2{}, fa, cur);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        // this wave's DMA of chunk c+1 has landed; after the barrier every
+        // wave's has, and every wave has read all of chunk c
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kYounger) : "memory");
+        lds_barrier();
+        a_dma(base + T + 3, b_cur);  // into the buffer chunk c just freed
+        const int b_free = b_cur;
+        b_cur = b_nxt;
+        b_nxt = b_far;
+        b_far = b_free;
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(I0{}, b_cur, fa);
+        mma(t_c, I3{}, fb, cur);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
     };
     SW sa[TNW], sbs[TNW];
     auto block = [&](int sbx, const SW (&cur)[TNW], SW (&nxt)[TNW]) {
@@ -904,28 +895,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
         pstep(I3{}, base, cur);
     };
 
-    // prologue: chunks c0, c0+1 into LDS buffers 0, 1; chunks c0+2, c0+3 in
-    // flight in register sets 0, 1; code blocks c0 .. c0+2 in flight.
+    // prologue: code blocks c0 .. c0+2 and the DMA of chunks c0 .. c0+2 in
+    // flight (in the order the steady state expects); chunk c0 in LDS first.
 #pragma unroll
     for (int tt = 0; tt < TNW; ++tt) sa[tt] = load_scale_block<FMT>(rs[tt], soff, sb0);
-    a_issue(I0{}, c0);
-    if constexpr (kSets == 2) a_issue(I1{}, c0 + 1);
     w_issue(I0{}, c0);
+    a_dma(c0, 0);
     w_issue(I1{}, c0 + 1);
+    a_dma(c0 + 1, kBuf);
     w_issue(I2{}, c0 + 2);
-    a_store(I0{}, I0{});
-    if constexpr (kSets == 1) a_issue(I1{}, c0 + 1);
-    a_store(I1{}, I1{});
-    a_issue(I0{}, c0 + 2);
-    if constexpr (kSets == 2) a_issue(I1{}, c0 + 3);
+    a_dma(c0 + 2, 2 * kBuf);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kStage) : "memory");  // DMA of chunk c0
     lds_barrier();
-    if constexpr (kPrefetch) read_frags(I0{}, I0{}, fa);
+    read_frags(I0{}, b_cur, fa);
     int sb = sb0;
     for (; sb + 1 < sb1; sb += 2) {
         block(sb, sa, sbs);
         block(sb + 1, sbs, sa);
     }
     if (sb < sb1) block(sb, sa, sbs);
+    // no DMA may still write this workgroup's LDS after it exits
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
     for (int tt = 0; tt < TNW; ++tt)

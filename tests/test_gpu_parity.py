@@ -279,6 +279,27 @@ def test_repeat_runs_bit_identical(m, act):
     assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("m,N,K,fmt", [(129, 32924, 1024, 0), (256, 33024, 2048, 1), (200, 65600, 544, 0)])
+def test_prefill_more_tiles_than_cus_full_oracle(m, N, K, fmt, act):
+    # more than 256 output tiles of 128 x 256 (ragged m, N and K), with the
+    # K split the shape model picks and a workspace of random bytes
+    need = F.workspace_size(m, N, K, fmt)
+    _say("prefill > 256 tiles", m, N, K, fmt, act, need)
+    p = synth.make_random(m, N, K, fmt, seed=m + N + K + fmt, act=act)
+    wq, sq = F.upload(*F.repack(p.codes, p.scales, p.N, p.K, p.fmt))
+    A = _to_dev_a(p.a_bits, act)
+    ws = (torch.randint(0, 256, (need,), dtype=torch.uint8, generator=torch.Generator().manual_seed(3)).cuda()
+          if need else None)
+    ys = []
+    for _ in range(2):
+        C = F.gemm(A, wq, sq, p.N, p.K, p.fmt, workspace=ws)
+        torch.cuda.synchronize()
+        ys.append(_bits(C))
+    assert np.array_equal(ys[0], ys[1])
+    check_full(p, ys[0])
+
+
 def test_one_workspace_reused_across_shapes_and_calls():
     # split-K partial sums and arrival words live in the workspace: neither
     # uninitialized contents nor stale contents from a call of another shape

@@ -333,6 +333,39 @@ def test_gemm_writes_into_given_output_on_given_stream():
     check_full(p, _bits(out))
 
 
+def test_split_k_gemms_on_two_streams_with_own_workspaces():
+    # decode GEMMs whose K split is finished in-kernel, issued alternately on
+    # two streams (each with its own workspace) and many times in a row: the
+    # arrival words of one launch must never count another launch's
+    # workgroups; every result is bit-identical to a lone call
+    shapes = [(16, 10240, 8192, 0), (16, 8192, 28672, 1)]
+    probs, ref, bufs = [], [], []
+    for i, (m, N, K, fmt) in enumerate(shapes):
+        assert F.workspace_size(m, N, K, fmt) > 0, "expected a K split"
+        p = synth.make_random(m, N, K, fmt, seed=101 + i)
+        wq, sq = F.upload(*F.repack(p.codes, p.scales, p.N, p.K, p.fmt))
+        A = _to_dev_a(p.a_bits)
+        y = F.gemm(A, wq, sq, p.N, p.K, p.fmt)
+        torch.cuda.synchronize()
+        probs.append((p, A, wq, sq))
+        ref.append(_bits(y))
+        bufs.append(F.new_workspace(m, N, K, fmt))
+    check_sampled(probs[0][0], ref[0])
+    check_sampled(probs[1][0], ref[1])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    _say("two streams", shapes)
+    for rep in range(8):
+        for i in (0, 1):
+            p, A, wq, sq = probs[i]
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(F.gemm(A, wq, sq, p.N, p.K, p.fmt, workspace=bufs[i], stream=streams[i]))
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        for y in outs[i]:
+            assert np.array_equal(_bits(y), ref[i])
+
+
 def test_device_errors_are_status_codes():
     p = synth.make_random(16, 64, 64, 0, seed=6)
     wq, sq = F.upload(*F.repack(p.codes, p.scales, p.N, p.K, p.fmt))

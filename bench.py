@@ -88,7 +88,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true", help="skip the FP16-activation decode and prefill lines")
     ap.add_argument("--no-moe", action="store_true", help="skip the grouped MoE GEMM lines")
-    ap.add_argument("--no-blas", action="store_true", help="skip the BF16 hipBLASLt comparison")
+    ap.add_argument("--no-blas", action="store_true",
+                    help="skip the BF16 hipBLASLt comparison and the measured copy / GEMM ceilings")
     ap.add_argument("--no-quantize", action="store_true", help="skip the quantizer line")
     ap.add_argument("--native", action="store_true", help="also time the native FP4 path (opt-in)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -336,6 +337,46 @@ def blas_lines(args, torch, layers, per_layer, prefill, dev):
     return out
 
 
+def ceilings(torch, dev):
+    """Measured ceilings beside the nominal peaks: a 1 GiB device-to-device
+    copy (bytes read + written per second) and the BF16 matrix product of the
+    vendor library at 8192^3 (hipBLASLt through torch.matmul)."""
+    out = {}
+    x = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 20
+    e0.record()
+    for _ in range(n):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    out["copy_GB/s"] = round(2.0 * x.numel() / us / 1e3, 1)
+    out["copy_frac_hbm"] = round(out["copy_GB/s"] / HBM_PEAK_GBS, 4)
+    del x, y
+    gen = torch.Generator(device=dev).manual_seed(5)
+    a = torch.randn((8192, 8192), device=dev, generator=gen).to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device=dev, generator=gen).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    n = 10
+    e0.record()
+    for _ in range(n):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    out["bf16_gemm_8192_TFLOP/s"] = round(2.0 * 8192 ** 3 / us / 1e6, 1)
+    out["bf16_gemm_frac_mfma"] = round(out["bf16_gemm_8192_TFLOP/s"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    out["note"] = "copy: torch copy_ of 1 GiB; gemm: torch.matmul BF16 8192^3 (hipBLASLt)"
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def moe_lines(args, F, torch, synth, dev):
     """Grouped MoE GEMM at 16 and 256 tokens.  The expert weights are random
     packed bytes made on the device (the packed layout is a permutation of
@@ -502,6 +543,11 @@ def main():
                    "note": "weights of the decode layers; A drawn N(0,1) in BF16 with its own seed"}
         log(f"prefill m=256: {prefill['TFLOP/s']} TFLOP/s")
 
+    ceil = None
+    if not args.no_blas:
+        ceil = ceilings(torch, dev)
+        log(f"ceilings: copy {ceil['copy_GB/s']} GB/s, BF16 GEMM 8192^3 {ceil['bf16_gemm_8192_TFLOP/s']} TFLOP/s")
+
     blas = None
     if not args.no_blas:
         blas = blas_lines(args, torch, layers, per_layer, prefill, dev)
@@ -558,6 +604,7 @@ def main():
         "layers": per_layer,
         "prefill": prefill,
         "vs_hipblaslt_bf16": blas,
+        "measured_ceilings": ceil,
         "fp16": fp16,
         "native": native,
         "moe": moe,

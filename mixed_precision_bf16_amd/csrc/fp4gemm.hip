@@ -190,7 +190,7 @@ static PrefillShape pick_prefill(int fmt, int64_t M, int64_t N, int NT, int SB) 
     }
     t = PrefillShape{1, 8, 8, 2, 1};
     // Time model fit to MI355X (m = 256): one workgroup per CU at a time
-    // (eight waves, 232 VGPRs); a round of workgroups over the whole K takes
+    // (eight waves, 228 VGPRs); a round of workgroups over the whole K takes
     // about 17 ns per K element, so a K split S runs ceil(blocks * S / 256)
     // rounds of 1/S of that; a split also writes and reads S FP32 partials
     // per output (about 5 TB/s) and pays the reduce launch (about 5 us).

@@ -811,21 +811,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Products of step I of chunk position T with fragments a.  The dequant
-    // of tile tt+1 is placed before the products of tile tt and the scheduler
-    // is asked to alternate one matrix instruction with two vector
-    // instructions, so the dequant runs while the matrix core works.
-    auto mma = [&](auto t_c, auto i_c, const u32x4 (&a)[MBW], const SW (&sc)[TNW]) {
+    // Dequantized weight fragments of the current MFMA step (one per n-tile).
+    // Each step's products use them while the next step's codes are
+    // dequantized, and the scheduler is asked to alternate one matrix
+    // instruction with two vector instructions: the dequant runs while the
+    // matrix core works, inside each wave.
+    u32x4 wcur[TNW];
+    // Products of step I of chunk position T with fragments a and wcur, and
+    // the dequant of the next step (chunk position NT, step NI, its scales
+    // sn: the next 512-K block's after the last step of a block) into wcur.
+    auto mma = [&](auto t_c, auto i_c, const u32x4 (&a)[MBW], const SW (&sn)[TNW]) {
         constexpr int T = decltype(t_c)::value;
         constexpr int I = decltype(i_c)::value;
-        u32x4 wf[TNW];
-        wf[0] = dequant_step<FMT, T, I, ACT>(wr[T][0], sc[0]);
+        constexpr int NT = I == 3 ? (T + 1) % 4 : T;
+        constexpr int NI = (I + 1) % 4;
+        u32x4 wn[TNW];
 #pragma unroll
-        for (int tt = 0; tt < TNW; ++tt) {
-            if (tt + 1 < TNW) wf[tt + 1] = dequant_step<FMT, T, I, ACT>(wr[T][tt + 1], sc[tt + 1]);
+        for (int tt = 0; tt < TNW; ++tt) wn[tt] = dequant_step<FMT, NT, NI, ACT>(wr[NT][tt], sn[tt]);
 #pragma unroll
-            for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = mfma<ACT>(wf[tt], a[mb], acc[tt][mb]);
-        }
+        for (int tt = 0; tt < TNW; ++tt)
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = mfma<ACT>(wcur[tt], a[mb], acc[tt][mb]);
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt) wcur[tt] = wn[tt];
     };
     auto interleave = [] {
         __builtin_amdgcn_sched_group_barrier(0x100, MBW, 0);  // next step's fragment reads first
@@ -851,8 +859,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
     // of the last block whose results are never used.)
     constexpr int kYounger = kStage;
     // chunk c = base + T (T = c % 4, also its code-ring slot); fa holds step
-    // 0's fragments on entry
-    auto pstep = [&](auto t_c, int base, const SW (&cur)[TNW]) {
+    // 0's fragments and wcur its dequantized weights on entry; nxt are the
+    // next block's scales (used by the dequant ahead of the block's end)
+    auto pstep = [&](auto t_c, int base, const SW (&cur)[TNW], const SW (&nxt)[TNW]) {
         constexpr int T = decltype(t_c)::value;
         w_issue(std::integral_constant<int, (T + 3) % 4>{}, base + T + 3);
         __builtin_amdgcn_sched_barrier(0);
@@ -879,7 +888,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
         b_far = b_free;
         __builtin_amdgcn_sched_barrier(0);
         read_frags(I0{}, b_cur, fa);
-        mma(t_c, I3{}, fb, cur);
+        if constexpr (T == 3) mma(t_c, I3{}, fb, nxt);
+        else mma(t_c, I3{}, fb, cur);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -889,10 +899,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
         const int nsb = min(sbx + 1, sb1 - 1);
 #pragma unroll
         for (int tt = 0; tt < TNW; ++tt) nxt[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
-        pstep(I0{}, base, cur);
-        pstep(I1{}, base, cur);
-        pstep(I2{}, base, cur);
-        pstep(I3{}, base, cur);
+        pstep(I0{}, base, cur, nxt);
+        pstep(I1{}, base, cur, nxt);
+        pstep(I2{}, base, cur, nxt);
+        pstep(I3{}, base, cur, nxt);
     };
 
     // prologue: code blocks c0 .. c0+2 and the DMA of chunks c0 .. c0+2 in
@@ -908,6 +918,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kStage) : "memory");  // DMA of chunk c0
     lds_barrier();
     read_frags(I0{}, b_cur, fa);
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt) wcur[tt] = dequant_step<FMT, 0, 0, ACT>(wr[0][tt], sa[tt]);
     int sb = sb0;
     for (; sb + 1 < sb1; sb += 2) {
         block(sb, sa, sbs);

@@ -40,12 +40,15 @@ static int64_t a_row_block(int64_t M) {
     return 128;  // prefill m-block
 }
 
-// Tuning override, read on every call so that a tuning run can change it.
+// Tuning override, read once per process.
 static DecodeShape decode_override() {
-    DecodeShape d{0, 0, 0, 0};
-    const char* e = getenv("FP4GEMM_DECODE");
-    if (e && *e) sscanf(e, "%d,%d,%d,%d", &d.tn, &d.nwn, &d.nwk, &d.s);
-    return d;
+    static const DecodeShape ov = [] {
+        DecodeShape d{0, 0, 0, 0};
+        const char* e = getenv("FP4GEMM_DECODE");
+        if (e && *e) sscanf(e, "%d,%d,%d,%d", &d.tn, &d.nwn, &d.nwk, &d.s);
+        return d;
+    }();
+    return ov;
 }
 
 static bool decode_compiled(int MB, const DecodeShape& d);
@@ -158,11 +161,15 @@ static void launch_reduce(int act, const float* P, void* C, int64_t total, int S
         reduce_partials<1><<<grid, block, 0, s>>>(P, (uint16_t*)C, total, S, alpha);
 }
 
+// Tuning override, read once per process.
 static PrefillShape prefill_override() {
-    PrefillShape t{0, 0, 0, 0, 1};
-    const char* e = getenv("FP4GEMM_PREFILL");
-    if (e && *e) sscanf(e, "%d,%d,%d,%d,%d", &t.wm, &t.wn, &t.mbw, &t.tnw, &t.s);
-    return t;
+    static const PrefillShape ov = [] {
+        PrefillShape t{0, 0, 0, 0, 1};
+        const char* e = getenv("FP4GEMM_PREFILL");
+        if (e && *e) sscanf(e, "%d,%d,%d,%d,%d", &t.wm, &t.wn, &t.mbw, &t.tnw, &t.s);
+        return t;
+    }();
+    return ov;
 }
 
 static bool prefill_compiled(const PrefillShape& t) {

@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true", help="skip the FP16-activation decode and prefill lines")
     ap.add_argument("--no-moe", action="store_true", help="skip the grouped MoE GEMM lines")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the MXFP4 decode sweep and the ragged-shape roofline fractions")
     ap.add_argument("--no-blas", action="store_true",
                     help="skip the BF16 hipBLASLt comparison and the measured copy / GEMM ceilings")
     ap.add_argument("--no-quantize", action="store_true", help="skip the quantizer line")
@@ -377,6 +379,58 @@ def ceilings(torch, dev):
     return out
 
 
+def config_lines(args, F, torch, dev):
+    """Roofline fractions of the MXFP4 decode sweep (m = 1, 4, 8, 16 at
+    8192 x 28672 and 57344 x 8192) and of the ragged NVFP4 set (m = 1, 7, 33,
+    100, 255; N = 1000, 8200; K = 8192).  Weights are random packed bytes on
+    the device with valid scale bytes (E8M0 121 .. 129, E4M3 0x18 .. 0x48):
+    the timing does not depend on the values; the GPU tests check these
+    shapes against the oracle.  t_roof = max(bytes / 8 TB/s, flops /
+    2.5 PFLOP/s); frac = t_roof / t."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(91)
+    lib = F.lib()
+    stream = F._c_vp(torch.cuda.current_stream().cuda_stream)
+
+    def run(N, K, fmt, ms, lo, hi):
+        nw, ns = F.repack_size(N, K, fmt)
+        R = max(2, math.ceil(ROTATE_BYTES / (nw + ns)))
+        copies = [(torch.randint(0, 256, (nw,), dtype=torch.uint8, device=dev, generator=gen),
+                   torch.randint(lo, hi + 1, (ns,), dtype=torch.uint8, device=dev, generator=gen)) for _ in range(R)]
+        G = 16 if fmt == 0 else 32
+        rows = []
+        for m in ms:
+            a = torch.randn((m, K), device=dev, generator=gen).to(torch.bfloat16)
+            c = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+            ws = F.new_workspace(m, N, K, fmt, device=dev)
+            wsb = ws.numel() if ws is not None else 0
+            argv = [(F._dev_ptr(a), F._dev_ptr(wq), F._dev_ptr(sq), F._dev_ptr(c), m, N, K, fmt, F._dev_ptr(ws), wsb,
+                     stream) for wq, sq in copies]
+
+            def call(s_, argv=argv):
+                st = lib.fp4_gemm(*argv[s_ % len(argv)])
+                if st:
+                    F._check(st, "fp4_gemm")
+            for s_ in range(5):
+                call(s_)
+            us = timed(call, max(30, 2 * R))
+            b = algorithmic_bytes(m, N, K, G)
+            fl = 2.0 * m * N * K
+            t_roof = max(b / (HBM_PEAK_GBS * 1e3), fl / (MFMA_BF16_PEAK_TFLOPS * 1e6))
+            rows.append({"m": m, "N": N, "K": K, "us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
+                         "TFLOP/s": round(fl / us / 1e6, 1),
+                         "bound": "hbm" if b / (HBM_PEAK_GBS * 1e3) >= fl / (MFMA_BF16_PEAK_TFLOPS * 1e6) else "mfma",
+                         "frac": round(t_roof / us, 4)})
+        del copies
+        torch.cuda.empty_cache()
+        return rows
+
+    mx = run(8192, 28672, 1, (1, 4, 8, 16), 121, 129) + run(57344, 8192, 1, (1, 4, 8, 16), 121, 129)
+    rg = run(1000, 8192, 0, (1, 7, 33, 100, 255), 0x18, 0x48) + run(8200, 8192, 0, (1, 7, 33, 100, 255), 0x18, 0x48)
+    return {"mxfp4_decode": mx, "ragged_nvfp4": rg,
+            "note": "frac = max(bytes / 8 TB/s, flops / 2.5 PFLOP/s) / measured time per launch"}
+
+
 def moe_lines(args, F, torch, synth, dev):
     """Grouped MoE GEMM at 16 and 256 tokens.  The expert weights are random
     packed bytes made on the device (the packed layout is a permutation of
@@ -554,6 +608,11 @@ def main():
         log("hipBLASLt bf16: fp4 speed-up m=16 mean " + str(blas.get("mean_speedup_m16")) + ", m=256 mean "
             + str(blas.get("mean_speedup_m256")))
 
+    cfg = None
+    if not args.no_configs:
+        cfg = config_lines(args, F, torch, dev)
+        log("mxfp4 decode frac: " + ", ".join(f"m={r['m']} {r['N']}x{r['K']} {r['frac']}" for r in cfg["mxfp4_decode"]))
+
     fp16 = None
     if not args.no_fp16:
         fp16 = fp16_lines(args, F, torch, layers, A, WS, dev, m)
@@ -605,6 +664,7 @@ def main():
         "prefill": prefill,
         "vs_hipblaslt_bf16": blas,
         "measured_ceilings": ceil,
+        "other_configs": cfg,
         "fp16": fp16,
         "native": native,
         "moe": moe,

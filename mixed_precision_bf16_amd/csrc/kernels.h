@@ -322,6 +322,7 @@ __device__ __forceinline__ void split_finish(const float* P, uint16_t* __restric
         case 2: split_sum<ACT, kThreads, 2>(P, C, M, N, S, m_begin, m_end, n_begin, n_end, alpha); break;
         case 4: split_sum<ACT, kThreads, 4>(P, C, M, N, S, m_begin, m_end, n_begin, n_end, alpha); break;
         case 8: split_sum<ACT, kThreads, 8>(P, C, M, N, S, m_begin, m_end, n_begin, n_end, alpha); break;
+        case 16: split_sum<ACT, kThreads, 16>(P, C, M, N, S, m_begin, m_end, n_begin, n_end, alpha); break;
         default: split_sum<ACT, kThreads, 0>(P, C, M, N, S, m_begin, m_end, n_begin, n_end, alpha); break;
     }
 }

@@ -300,6 +300,21 @@ def test_prefill_more_tiles_than_cus_full_oracle(m, N, K, fmt, act):
     check_full(p, ys[0])
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("m,N,K,fmt", [(33, 33000, 1024, 0), (64, 32768, 544, 1), (48, 40000, 2048, 0)])
+def test_wide_layer_mid_m_full_oracle(m, N, K, fmt, act):
+    # 33 <= m <= 64 on a layer of at least 128 groups of 256 columns runs the
+    # prefill kernel with 64-row tiles over the whole K (no workspace)
+    assert F.workspace_size(m, N, K, fmt) == 0
+    _say("wide mid m", m, N, K, fmt, act)
+    p = synth.make_random(m, N, K, fmt, seed=7 * m + N + K + fmt, act=act)
+    wq, sq = F.upload(*F.repack(p.codes, p.scales, p.N, p.K, p.fmt))
+    A = _to_dev_a(p.a_bits, act)
+    C = F.gemm(A, wq, sq, p.N, p.K, p.fmt)
+    torch.cuda.synchronize()
+    check_full(p, _bits(C))
+
+
 def test_one_workspace_reused_across_shapes_and_calls():
     # split-K partial sums and arrival words live in the workspace: neither
     # uninitialized contents nor stale contents from a call of another shape

@@ -302,6 +302,12 @@ def test_workspace_size_is_a_split_k_partial_buffer():
         assert b == S * 4 * m * N, (m, N, K, b)
     assert F.workspace_size(256, 57344, 8192, 0) == 0
     assert F.new_workspace(1000, 57344, 8192, 0) is None
+    # 33 <= m <= 64 on a layer of >= 128 groups of 256 columns: whole-K prefill
+    # tiles, no workspace; the same m on a narrow layer keeps the decode kernel
+    for m in (33, 48, 64):
+        assert F.workspace_size(m, 57344, 8192, 0) == 0
+        assert F.workspace_size(m, 32768, 544, 1) == 0
+    assert F.workspace_size(48, 8192, 8192, 0) > 0
 
 
 def test_gemm_rejects_small_or_misaligned_workspace_before_any_hip_call():

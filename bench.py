@@ -545,6 +545,15 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     dom_us = e0.elapsed_time(e1) / n_dom * 1e3
+    # the same launches with events around each one: median and minimum
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dom)]
+    for s, (a, b) in enumerate(ev):
+        a.record()
+        calls[dom][s % dl.R]()
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    dom_median, dom_min = per[len(per) // 2], per[0]
     gbs = bytes_step / (ms_step * 1e-3) / 1e9
     dom_bytes = algorithmic_bytes(m, dl.N, dl.K, dl.G)
     dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
@@ -659,6 +668,7 @@ def main():
         "roofline": {"kernel": "gemm_decode (gate_up, m=16)", "bound": "hbm", "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_us, 2), "launches": n_dom,
+                     "us_per_launch_median": round(dom_median, 2), "us_per_launch_min": round(dom_min, 2),
                      "traffic": measured_traffic()},
         "layers": per_layer,
         "prefill": prefill,

@@ -408,9 +408,11 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
                                                              float alpha, uint32_t tag, MoeArgs moe = MoeArgs{}) {
     typedef u32x4 SW;
     constexpr int kRows = 16 * MB;  // activation rows; one 1 KiB load per row per block
-    // Activation load instructions per wave per block.  When NWN does not
-    // divide the row count, the surplus loads repeat the last row: they
-    // write the same bytes to the same LDS slot as its first load.
+    // Activation load instructions per wave per block (row wn + NWN u).  When
+    // NWN does not divide the row count, a wave's last slot may fall past
+    // the last row: it loads and stores nothing (every row has exactly one
+    // owner, and each load costs the CU's vector-memory path as much as a
+    // code load does).
     constexpr int QB = (kRows + NWN - 1) / NWN;
     constexpr int kBuf = MB * 4096;  // one chunk: 16*MB rows x 128 K x 2 B
     constexpr int kBlk = 4 * kBuf;     // one 512-K block
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
         const int row = min(wn + NWN * u, kRows - 1);
-        alive[u] = row < M;
+        alive[u] = wn + NWN * u < kRows && row < M;
         aoff[u] = (uint32_t)(row * K + 8 * lane) * 2u;
         if constexpr (MOE) {
             // gathered row; an id outside [0, a_div * a_rows) reads zeros

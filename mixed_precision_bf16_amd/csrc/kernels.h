@@ -380,11 +380,12 @@ __device__ __forceinline__ int moe_find_block(const MoeArgs& moe, int item, int 
 // different n-tiles (TN each), so one activation chunk in LDS feeds
 // TN*NWN tiles: each activation byte crosses the L1/L2 path once per
 // workgroup instead of once per wave, and the loads that bring it in read
-// whole 128-byte lines (8 rows x 128 bytes per wave instruction).  The NWK
+// whole 128-byte lines (1 KiB of one row per wave instruction).  The NWK
 // groups split the workgroup's K range and are summed through LDS in a fixed
 // order.  Narrow layers also split K over S workgroups: each writes FP32
-// partial sums to the caller's workspace and reduce_partials adds them in a
-// fixed order (no atomics, deterministic).
+// partial sums to the caller's workspace and the group's last workgroup to
+// arrive adds them in the fixed order s = 0, 1, ... (split-K fixup above;
+// the only atomics count arrivals, so results are deterministic).
 //
 // Pipeline.  Code blocks stream through a four-slot register ring, three
 // 128-K chunks ahead of the multiply.  Activations move one 512-K scale block

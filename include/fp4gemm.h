@@ -40,7 +40,9 @@
  *   - "device" pointers must be HIP device memory on the current device;
  *     "host" pointers must be ordinary host memory.
  *   - Functions are reentrant and thread-safe; the only global state is a
- *     per-device "is gfx950" cache.
+ *     per-device "is gfx950" cache, an atomic launch counter that tags the
+ *     split-K arrival words, and the tuning overrides FP4GEMM_DECODE /
+ *     FP4GEMM_PREFILL, read from the environment once per process.
  */
 #ifndef FP4GEMM_H
 #define FP4GEMM_H

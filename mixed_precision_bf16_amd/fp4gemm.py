@@ -144,6 +144,14 @@ def _dev_ptr(t):
     return _c_vp(t.data_ptr()) if t is not None else _c_vp(0)
 
 
+def _on_device_of(ref, **tensors):
+    """Raise ValueError unless every given tensor (None allowed) is a CUDA
+    tensor on ref's device: a host pointer handed to a kernel would fault."""
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != ref.device):
+            raise ValueError(f"{name} must be a CUDA tensor on {ref.device}")
+
+
 def _stream_handle(stream):
     import torch
     if stream is None:
@@ -178,6 +186,9 @@ def gemm(A, wq, sq, N: int, K: int, fmt: int, out=None, workspace=None, stream=N
         out = torch.empty((m, N), dtype=A.dtype, device=A.device)
     elif out.shape != (m, N) or out.dtype != A.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor [m][N] of A's dtype")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
+    _on_device_of(A, wq=wq, sq=sq, out=out, workspace=workspace)
     wsb = workspace_size(m, N, K, fmt)
     if wsb and workspace is None:
         workspace = torch.zeros(wsb, dtype=torch.uint8, device=A.device)
@@ -222,6 +233,7 @@ def dequant(wq, sq, N: int, K: int, fmt: int, out=None, stream=None, dtype=None)
         out = torch.empty((N, K), dtype=dtype, device=wq.device)
     elif out.shape != (N, K) or out.dtype != dtype or not out.is_cuda or not out.is_contiguous():
         raise ValueError("out must be a contiguous CUDA tensor [N][K] of the requested dtype")
+    _on_device_of(wq, sq=sq, out=out)
     fn = lib().fp4_dequant if dtype == torch.bfloat16 else lib().fp4_dequant_f16
     _check(fn(_dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), N, K, fmt, _stream_handle(stream)), "fp4_dequant")
     return out
@@ -260,6 +272,8 @@ def moe_gemm(A, wq, sq, sorted_ids, expert_offsets, N: int, K: int, fmt: int, E:
         out = torch.zeros((out_rows, N), dtype=torch.bfloat16, device=A.device)
     elif out.shape != (out_rows, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous bfloat16 tensor [out_rows][N]")
+    _on_device_of(A, wq=wq, sq=sq, sorted_ids=sorted_ids, expert_offsets=expert_offsets,
+                  topk_weights=topk_weights, out=out)
     _check(lib().fp4_moe_gemm(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(sorted_ids), _dev_ptr(expert_offsets),
                               _dev_ptr(topk_weights), _dev_ptr(out), A.shape[0], a_div, out_rows,
                               sorted_ids.numel(), E, N, K, fmt, _stream_handle(stream)), "fp4_moe_gemm")

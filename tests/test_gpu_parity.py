@@ -381,6 +381,26 @@ def test_split_k_gemms_on_two_streams_with_own_workspaces():
             assert np.array_equal(_bits(y), ref[i])
 
 
+def test_binding_rejects_tensors_off_the_device():
+    # A host pointer handed to a kernel would fault: the binding refuses it
+    # before any launch.
+    p = synth.make_random(16, 64, 512, 0, seed=7)
+    wq, sq = F.upload(*F.repack(p.codes, p.scales, p.N, p.K, p.fmt))
+    A = _to_dev_a(p.a_bits)
+    with pytest.raises(ValueError):
+        F.gemm(A, wq, sq, p.N, p.K, p.fmt, out=torch.empty((16, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        F.gemm(A, wq, sq, p.N, p.K, p.fmt, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        F.gemm(A, wq.cpu(), sq, p.N, p.K, p.fmt)
+    with pytest.raises(ValueError):
+        F.dequant(wq, sq.cpu(), p.N, p.K, p.fmt)
+    torch.cuda.synchronize()
+    y = F.gemm(A, wq, sq, p.N, p.K, p.fmt)  # the valid call still works
+    torch.cuda.synchronize()
+    assert y.shape == (16, 64)
+
+
 def test_device_errors_are_status_codes():
     p = synth.make_random(16, 64, 64, 0, seed=6)
     wq, sq = F.upload(*F.repack(p.codes, p.scales, p.N, p.K, p.fmt))

@@ -205,6 +205,9 @@ def act_bits_to_f64(bits: np.ndarray, act: str = "bf16") -> np.ndarray:
     raise ValueError(f"unknown activation type {act}")
 
 
+GEMM_CHUNK_ROWS = 2048
+
+
 def gemm_reference(a_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray,
                    K: int, fmt: int, act: str = "bf16"):
     """Y_ref[i][n] = sum_k a[i][k] w[n][k] and B[i][n] = sum_k |a[i][k] w[n][k]|.
@@ -213,13 +216,25 @@ def gemm_reference(a_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray,
     is below K * 2^-53 * B, negligible against the tolerance).  `act` names
     the type of the activation bits (BF16 or FP16).  Returns (y_ref, bound),
     each [m][N].
+
+    The weight rows are dequantized and multiplied GEMM_CHUNK_ROWS at a time
+    (a plain loop over N that only bounds memory: every output column is the
+    same dot product over all of K whatever the chunking).
     """
     a = act_bits_to_f64(a_bits, act)
     if a.ndim != 2 or a.shape[1] != K:
         raise ValueError("A must be [m][K]")
-    w = dequant_weights(codes, scales, K, fmt)
-    y = a @ w.T
-    bound = np.abs(a) @ np.abs(w).T
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    N = codes.shape[0]
+    y = np.empty((a.shape[0], N), dtype=np.float64)
+    bound = np.empty((a.shape[0], N), dtype=np.float64)
+    abs_a = np.abs(a)
+    for n0 in range(0, N, GEMM_CHUNK_ROWS):
+        n1 = min(N, n0 + GEMM_CHUNK_ROWS)
+        w = dequant_weights(codes[n0:n1], scales[n0:n1], K, fmt)
+        y[:, n0:n1] = a @ w.T
+        bound[:, n0:n1] = abs_a @ np.abs(w).T
     return y, bound
 
 

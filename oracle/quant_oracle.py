@@ -22,9 +22,11 @@ Readings (the pages leave these open):
   (the block maximum lands on the largest grid value), saturated to 448 and
   floored at the smallest positive E4M3 (2^-9), so it is never zero.
 * MXFP4 block scale = 2^(floor(log2(amax / alpha)) - 2) (the OCP MX rule for
-  E2M1, whose largest exponent is 2), byte clamped to 0 .. 254; byte 0
-  (amax / alpha below 2^-125, including an all-zero block) marks a zero
-  block: all its codes are 0.
+  E2M1, whose largest exponent is 2), byte clamped to 0 .. 254.  Byte 0 is
+  the scale 2^-127 like any other byte (it covers every amax / alpha below
+  2^-124, including an all-zero block); its block is divided and rounded
+  like every other block (section 2.2 of the article), so only elements
+  that round to zero get code 0.
 * An infinite amax gives the largest scale (E4M3 448, E8M0 byte 254).
 * Effective scale S = alpha * scale; quotient q = |x| / S; nearest grid
   value with ties to the even mantissa bit (round-to-nearest-even), values
@@ -93,13 +95,11 @@ def quantize_reference(w_bits: np.ndarray, fmt: int, alpha: float = 1.0):
         e = np.where(t > 0, ex - 1 - 2, -127)
         e = np.where(np.isinf(t), 127, e)
         sb = np.clip(e + 127, 0, 254).astype(np.uint8)
-        sval = np.exp2(sb.astype(np.float64) - 127.0).astype(np.float32)
+        sval = np.exp2(sb.astype(np.float64) - 127.0).astype(np.float32)   # byte 0: 2^-127, an FP32 subnormal
     S = (a32 * sval).astype(np.float32)                         # [N][K/G]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = (np.abs(blocks) / S[..., None]).astype(np.float32)
     mag = nearest_e2m1(q)
-    if fmt == 1:
-        mag = np.where((sb == 0)[..., None], 0, mag)                  # byte 0 marks a zero block
     neg = np.signbit(blocks) & (mag != 0) & ~np.isnan(blocks)
     code = (mag | np.where(neg, 8, 0)).reshape(N, K).astype(np.uint8)
     packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)

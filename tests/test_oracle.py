@@ -437,3 +437,28 @@ def test_planted_mistake_is_caught(name, over):
 
 def test_package_exports():
     assert oracle.gemm_reference is O.gemm_reference
+
+
+def test_gemm_reference_chunks_cover_every_row():
+    """The oracle dequantizes and multiplies the weight rows in chunks of
+    GEMM_CHUNK_ROWS: columns on both sides of every chunk boundary and in
+    the ragged last chunk equal the math.fsum brute force of their dot
+    products."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    m, K, fmt = 2, 32, 0
+    N = 2 * O.GEMM_CHUNK_ROWS + 37
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0x20, 0x48, size=(N, K // 16)).astype(np.uint8)
+    a_bits = _a_bits(rng.standard_normal((m, K)).astype(np.float32).tolist())
+    a_vals = torch.from_numpy(a_bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    y, b = O.gemm_reference(a_bits, codes, scales, K, fmt)
+    assert y.shape == (m, N) and b.shape == (m, N)
+    C = O.GEMM_CHUNK_ROWS
+    cols = [0, 1, C - 1, C, C + 1, 2 * C - 1, 2 * C, N - 2, N - 1]
+    unpacked = _codes_from_packed(codes[cols].tolist(), K)
+    for ci, n in enumerate(cols):
+        for i in range(m):
+            terms = [float(a_vals[i, k]) * float(_page_e2m1_fraction(unpacked[ci][k]))
+                     * float(_lib_scale_fraction(int(scales[n][k // 16]), fmt)) for k in range(K)]
+            s, bb = math.fsum(terms), math.fsum(abs(t) for t in terms)
+            assert abs(y[i, n] - s) <= 1e-12 * bb and abs(b[i, n] - bb) <= 1e-12 * bb, (i, n)

@@ -8,8 +8,10 @@
   quantize back to exactly those codes and scales (both formats).
 * The zero-block rule (positive scale, zero codes), saturation, no negative
   zero, and the error bound |w - dequant| <= S * (half the local grid gap).
+* MXFP4 blocks below 2^-124 (scale byte 0 = 2^-127): exact rational block
+  scaling, and the fixed point at scale bytes 0, 1, 2.
 Planted mistakes (ties away from zero, scale = amax, sign dropped, E8M0
-exponent rounded up) each fail a pin.
+exponent rounded up, E8M0 byte 0 flushing its block) each fail a pin.
 """
 
 from fractions import Fraction
@@ -68,6 +70,7 @@ def pin_fixed_point(q):
             sb = rng.integers(0x08, 0x50, size=(N, K // G)).astype(np.uint8)   # normal E4M3
         else:
             sb = rng.integers(110, 140, size=(N, K // G)).astype(np.uint8)
+            sb[0] = [0, 1, 2, 0]        # the smallest E8M0 scales: 2^-127 (byte 0), 2^-126, 2^-125
         packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
         w = O.dequant_weights(packed, sb, K, fmt)
         c2, s2 = q.quantize_reference(O.bf16_bits_of_exact(w), fmt)
@@ -108,8 +111,53 @@ def pin_error_bound(q):
         assert np.all(np.abs(d[sat]) == 6 * S[sat])
 
 
+def _frac_floor_log2(x: Fraction) -> int:
+    e = x.numerator.bit_length() - x.denominator.bit_length()
+    while Fraction(2) ** e > x:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= x:
+        e += 1
+    return e
+
+
+def pin_tiny_mx_blocks_exact(q):
+    """MXFP4 blocks whose maximum lies below 2^-124 (scale byte 0 = 2^-127):
+    exact rational arithmetic of block scaling (divide by the block's scale,
+    then round to the nearest grid value, ties to the even code, saturating
+    at 6; mhpq.cn article sections 2.1 and 2.2) with the scale
+    2^max(floor(log2 amax) - 2, -127).  A non-zero element that does not
+    round to zero keeps a non-zero code."""
+    amaxes = [2.0 ** -126, 1.5 * 2.0 ** -125, 1.8984375 * 2.0 ** -125, 2.0 ** -124, 1.75 * 2.0 ** -127]
+    rng = np.random.Generator(np.random.PCG64(5))
+    w = np.zeros((len(amaxes), 32), np.float32)
+    for i, a in enumerate(amaxes):
+        w[i, 0] = a
+        w[i, 1:] = (rng.uniform(-1, 1, size=31) * a).astype(np.float32)
+        w[i, 1:4] = [-a / 2, a / 3, 2.0 ** -133]            # a midpoint-ish value and the smallest BF16
+    bits = _bf16_bits(w)
+    x = O.bf16_bits_to_f64(bits)
+    c, s = q.quantize_reference(bits, 1)
+    codes = O.unpack_codes(c, 32)
+    for i in range(len(amaxes)):
+        fr = [Fraction(float(v)) for v in x[i]]
+        amax = max(abs(v) for v in fr)
+        e = max(_frac_floor_log2(amax) - 2, -127)
+        assert int(s[i, 0]) == e + 127, (i, s[i, 0], e)
+        S = Fraction(2) ** e
+        for k, v in enumerate(fr):
+            qv = abs(v) / S
+            d = [abs(g - qv) for g in GRID]
+            best = [j for j in range(8) if d[j] == min(d)]
+            mag = best[0] if len(best) == 1 else [j for j in best if j % 2 == 0][0]
+            if qv > 6:
+                mag = 7
+            want = mag | (8 if (v < 0 and mag) else 0)
+            assert codes[i, k] == want, (i, k, float(v), codes[i, k], want)
+    assert np.all(codes[:, 0] != 0), "each block maximum keeps a non-zero code"
+
+
 ALL_PINS = [pin_e4m3_encode_library, pin_nearest_grid_bruteforce, pin_fixed_point, pin_zero_block_and_signs,
-            pin_error_bound]
+            pin_error_bound, pin_tiny_mx_blocks_exact]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -185,8 +233,20 @@ def _mut_e8m0_ceil(w_bits, fmt, alpha=1.0):
     return c, s
 
 
+def _mut_byte0_flush(w_bits, fmt, alpha=1.0):
+    # a reading that zeroes every code of a block whose E8M0 scale byte is 0
+    c, s = Q.quantize_reference(w_bits, fmt, alpha)
+    if fmt == 1:
+        K = c.shape[1] * 2
+        blk = np.repeat(s == 0, 16, axis=1)
+        c = np.where(blk, 0, c).astype(np.uint8)
+        assert c.shape[1] * 2 == K
+    return c, s
+
+
 @pytest.mark.parametrize("name,over", [
     ("ties away from zero", {"nearest_e2m1": _mut_ties_away}),
+    ("E8M0 byte 0 flushes its block", {"quantize_reference": _mut_byte0_flush}),
     ("scale = amax", {"quantize_reference": _mut_scale_amax}),
     ("sign dropped", {"quantize_reference": _mut_no_sign}),
     ("E8M0 exponent rounded up", {"quantize_reference": _mut_e8m0_ceil}),

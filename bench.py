@@ -132,31 +132,55 @@ def make_call(F, torch, layer, A, C, r, ws, entry="fp4_gemm"):
     return call
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(decode_layers_probs):
     """The oracle as it stands (float64 NumPy: dequant + library matmul) on a
-    bounded sample: m = 16 against the first 8192 rows of the gate/up weights."""
+    bounded sample: m = 16 against the first 8192 rows of the gate/up weights,
+    on all host cores available to the process (BLAS threads set to match)."""
     import oracle
+    cores = len(os.sched_getaffinity(0))
+    blas = {"vendor": "unknown", "threads": None}
+    limiter = None
     try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            blas = {"vendor": info[0].get("internal_api", "unknown"),
+                    "threads": max(p.get("num_threads", 1) for p in info)}
     except Exception:  # noqa: BLE001
-        blas_threads = 1
+        pass
     p = decode_layers_probs[2]
     rows = 8192
     codes, scales = p.codes[:rows], p.scales[:rows]
     reps, times = 0, []
     t_start = time.perf_counter()
-    while reps < 3 or (time.perf_counter() - t_start < 10.0 and reps < 30):
-        t0 = time.perf_counter()
-        oracle.gemm_reference(p.a_bits, codes, scales, p.K, p.fmt)
-        times.append(time.perf_counter() - t0)
-        reps += 1
+    try:
+        while reps < 3 or (time.perf_counter() - t_start < 10.0 and reps < 30):
+            t0 = time.perf_counter()
+            oracle.gemm_reference(p.a_bits, codes, scales, p.K, p.fmt)
+            times.append(time.perf_counter() - t0)
+            reps += 1
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
     t = float(np.mean(times))
     b = algorithmic_bytes(p.m, rows, p.K, p.group)
-    return {"value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+    return {"value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "blas_vendor": blas["vendor"], "blas_threads": blas["threads"],
             "sample": f"m=16 x first {rows} rows of the gate_up weights (K={p.K}), float64 NumPy dequant + "
-                      f"matmul, mean of {reps} runs ({t:.2f} s each); elementwise dequant runs on one thread, "
-                      f"the matmul on {blas_threads} BLAS threads",
+                      f"matmul, mean of {reps} runs ({t:.2f} s each); the elementwise dequant runs on one "
+                      f"thread, the matmul on {blas['threads']} {blas['vendor']} threads "
+                      f"({cores} cores in the process's affinity set)",
             "seconds_per_run": round(t, 3)}
 
 

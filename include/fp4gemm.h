@@ -41,8 +41,10 @@
  *     "host" pointers must be ordinary host memory.
  *   - Functions are reentrant and thread-safe; the only global state is a
  *     per-device "is gfx950" cache, an atomic launch counter that tags the
- *     split-K arrival words, and the tuning overrides FP4GEMM_DECODE /
- *     FP4GEMM_PREFILL, read from the environment once per process.
+ *     split-K arrival words, a 64-entry cache of the kernel shape chosen per
+ *     (m, N, K, format) (behind a mutex), and the tuning overrides
+ *     FP4GEMM_DECODE / FP4GEMM_PREFILL, read from the environment once per
+ *     process.
  */
 #ifndef FP4GEMM_H
 #define FP4GEMM_H
@@ -108,14 +110,17 @@ int fp4_unpack(const uint8_t* wq, const uint8_t* sq, int64_t N, int64_t K, int f
 
 /* Workspace bytes fp4_gemm needs for this problem (a pure function of its
  * arguments; no device is queried).  The library may split K over S
- * workgroups (split-K, the Petit blog's section "Detailed performance
- * analysis" motivates it for the skinny decode case): each writes FP32
+ * workgroups (split-K; not described on the pages: a narrow layer at the
+ * decode batch m = 16 has too few 16-row output tiles to give each of the
+ * 256 compute units its own): each writes FP32
  * partial sums of its K range, which are added in a fixed order s = 0, 1, ...
  * For m <= 64 the last workgroup of each output group adds them (it finds out
  * through an 8-byte arrival word per group, after the partials); for m > 64 a
  * second kernel does.  The size is about S * m * N * 4 bytes, or 0 when no
  * split is chosen.  The contents need no initialization (the arrival words
- * carry a tag unique to each launch) and are not preserved between calls. */
+ * carry a tag unique to each launch, and the last workgroup of a group
+ * leaves its word at zero, so a call captured in a HIP graph can be
+ * replayed with its workspace) and are not preserved between calls. */
 int fp4_gemm_workspace_size(int64_t m, int64_t N, int64_t K, int format, size_t* bytes);
 
 /* Y = A . dequant(W)^T on `stream` (a hipStream_t; NULL = default stream).
@@ -186,7 +191,8 @@ int fp4_gemm_ex(const void* A, const void* wq, const void* sq, void* C, int64_t 
  *   NVFP4: scale = E4M3 round-to-nearest-even of (amax / 6) / alpha,
  *          saturated at 448 and at least 2^-9 (never zero);
  *   MXFP4: scale byte = clamp(floor(log2(amax / alpha)) - 2 + 127, 0, 254)
- *          (the OCP MX rule); byte 0 makes every code of the block 0;
+ *          (the OCP MX rule); byte 0 is the scale 2^-127 (any amax / alpha
+ *          below 2^-124) and its block is rounded like every other;
  *   code = nearest E2M1 value to |x| / (alpha * scale), ties to the even
  *   mantissa bit, saturating at +-6; no negative zero; NaN -> 0, +-Inf ->
  *   +-6 with the largest scale.

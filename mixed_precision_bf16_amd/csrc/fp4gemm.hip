@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "dispatch.h"
 #include "kernels.h"
@@ -226,24 +227,78 @@ static bool wide_mid_m(int64_t M, int NT) {
     return M > 32 && M <= 64 && (NT + 15) / 16 >= 128;
 }
 
-static int launch_gemm(int fmt, int act, const void* A, const void* wq, const void* sq, void* C, void* ws, int M,
-                       int N, int K, int KB, int SB, int NT, float alpha, hipStream_t s) {
-    if (wide_mid_m(M, NT)) {
-        const PrefillShape t{1, 8, 4, 2, 1};
-        const bool ok = act == 0 ? launch_prefill_bf16(fmt, t, A, wq, sq, C, nullptr, M, N, K, KB, SB, NT, alpha, s)
-                                 : launch_prefill_f16(fmt, t, A, wq, sq, C, nullptr, M, N, K, KB, SB, NT, alpha, s);
+// The kernel, shape and K split chosen for one problem, and its workspace.
+struct GemmPlan {
+    enum Kind { kDecode, kPrefill, kPrefillMid } kind;
+    int MB;             // decode: 16-row activation blocks
+    DecodeShape d;      // decode shape and split
+    PrefillShape t;     // prefill shape and split
+    size_t ws_bytes;    // workspace fp4_gemm needs
+};
+
+static GemmPlan make_plan(int fmt, int64_t M, int64_t N, int64_t K) {
+    const int SB = int(padded_k(K) / kScaleBlockK), NT = int(padded_n(N) / kTileN);
+    GemmPlan p{};
+    if (wide_mid_m(M, NT)) {  // whole-K prefill tiles, no split
+        p.kind = GemmPlan::kPrefillMid;
+        p.t = PrefillShape{1, 8, 4, 2, 1};
+        p.ws_bytes = 0;
+    } else if (M <= 64) {
+        p.kind = GemmPlan::kDecode;
+        p.MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+        p.d = pick_decode(fmt, p.MB, M, N, NT, SB);
+        p.ws_bytes = decode_workspace_bytes(p.d, M, N, NT);
+    } else {
+        p.kind = GemmPlan::kPrefill;
+        p.t = pick_prefill(fmt, M, N, NT, SB);
+        p.ws_bytes = p.t.s > 1 ? (size_t)p.t.s * (size_t)M * (size_t)N * sizeof(float) : 0;
+    }
+    return p;
+}
+
+// Plans of recent problems, keyed by (m, N, K, format): a small direct-mapped
+// table behind a mutex, so a caller that repeats shapes (every decode step)
+// does not rerun the shape models.  No allocation after the first call.
+static GemmPlan cached_plan(int fmt, int64_t M, int64_t N, int64_t K) {
+    struct Entry {
+        int64_t m, n, k;
+        int fmt;
+        bool used;
+        GemmPlan plan;
+    };
+    constexpr int kEntries = 64;
+    static Entry table[kEntries];
+    static std::mutex mu;
+    const uint64_t h = ((uint64_t)M * 0x9E3779B97F4A7C15ull) ^ ((uint64_t)N * 0xC2B2AE3D27D4EB4Full) ^
+                       ((uint64_t)K * 0x165667B19E3779F9ull) ^ (uint64_t)fmt;
+    Entry& e = table[(h >> 32) % kEntries];
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (e.used && e.m == M && e.n == N && e.k == K && e.fmt == fmt) return e.plan;
+    }
+    const GemmPlan plan = make_plan(fmt, M, N, K);
+    std::lock_guard<std::mutex> lock(mu);
+    e = Entry{M, N, K, fmt, true, plan};
+    return plan;
+}
+
+static int launch_gemm(const GemmPlan& plan, int fmt, int act, const void* A, const void* wq, const void* sq,
+                       void* C, void* ws, int M, int N, int K, int KB, int SB, int NT, float alpha, hipStream_t s) {
+    if (plan.kind == GemmPlan::kPrefillMid) {
+        const bool ok = act == 0 ? launch_prefill_bf16(fmt, plan.t, A, wq, sq, C, nullptr, M, N, K, KB, SB, NT, alpha, s)
+                                 : launch_prefill_f16(fmt, plan.t, A, wq, sq, C, nullptr, M, N, K, KB, SB, NT, alpha, s);
         return ok ? FP4_OK : FP4_ERR_SHAPE;
     }
-    if (M <= 64) {
-        const int MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-        const DecodeShape d = pick_decode(fmt, MB, M, N, NT, SB);
+    if (plan.kind == GemmPlan::kDecode) {
+        const DecodeShape& d = plan.d;
         float* P = d.s > 1 ? static_cast<float*>(ws) : nullptr;
         const uint32_t tag = P ? next_split_tag() : 0u;
-        const bool ok = act == 0 ? launch_decode_bf16(fmt, MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, tag, s)
-                                 : launch_decode_f16(fmt, MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, tag, s);
+        const bool ok =
+            act == 0 ? launch_decode_bf16(fmt, plan.MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, tag, s)
+                     : launch_decode_f16(fmt, plan.MB, d, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, tag, s);
         return ok ? FP4_OK : FP4_ERR_SHAPE;
     }
-    const PrefillShape t = pick_prefill(fmt, M, N, NT, SB);
+    const PrefillShape& t = plan.t;
     float* P = t.s > 1 ? static_cast<float*>(ws) : nullptr;
     const bool ok = act == 0 ? launch_prefill_bf16(fmt, t, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, s)
                              : launch_prefill_f16(fmt, t, A, wq, sq, C, P, M, N, K, KB, SB, NT, alpha, s);
@@ -255,14 +310,7 @@ static int launch_gemm(int fmt, int act, const void* A, const void* wq, const vo
 // Workspace bytes of the kernel fp4_gemm picks for this problem.
 static size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
     if (M == 0) return 0;
-    const int SB = int(padded_k(K) / kScaleBlockK), NT = int(padded_n(N) / kTileN);
-    if (wide_mid_m(M, NT)) return 0;  // whole-K prefill tiles, no split
-    if (M > 64) {
-        const PrefillShape t = pick_prefill(fmt, M, N, NT, SB);
-        return t.s > 1 ? (size_t)t.s * (size_t)M * (size_t)N * sizeof(float) : 0;
-    }
-    const int MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    return decode_workspace_bytes(pick_decode(fmt, MB, M, N, NT, SB), M, N, NT);
+    return cached_plan(fmt, M, N, K).ws_bytes;
 }
 
 // alpha: finite, |alpha| in [2^-100, 2^100] or exactly 1 (checked by the entries).
@@ -284,7 +332,8 @@ static int gemm_impl(int act, const void* A, const void* wq, const void* sq, voi
          reinterpret_cast<uintptr_t>(C)) & 15)
         return FP4_ERR_SHAPE;
     if (round_up(m, a_row_block(m)) * K * 2 >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
-    const size_t need = gemm_workspace_bytes(m, N, K, format);
+    const GemmPlan plan = cached_plan(format, m, N, K);
+    const size_t need = plan.ws_bytes;
     if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15)))
         return FP4_ERR_WORKSPACE;
     st = check_device();
@@ -292,7 +341,7 @@ static int gemm_impl(int act, const void* A, const void* wq, const void* sq, voi
     const int64_t Np = padded_n(N), Kp = padded_k(K);
     const int KB = int(Kp / kChunkK), SB = int(Kp / kScaleBlockK), NT = int(Np / kTileN);
     (void)hipGetLastError();
-    st = launch_gemm(format, act, A, wq, sq, C, workspace, int(m), int(N), int(K), KB, SB, NT, alpha,
+    st = launch_gemm(plan, format, act, A, wq, sq, C, workspace, int(m), int(N), int(K), KB, SB, NT, alpha,
                      reinterpret_cast<hipStream_t>(stream));
     if (st != FP4_OK) return st;
     return launch_status();

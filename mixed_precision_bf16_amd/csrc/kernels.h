@@ -215,11 +215,14 @@ __device__ __forceinline__ u32x4 load_scale_block(__amdgpu_buffer_rsrc_t r, int 
 // order s = 0, 1, ... (device-coherent loads), scales by alpha and writes
 // the output.  Because every access to the partials and to the arrival word
 // is device-coherent, no cache-wide write-back or invalidate is needed.
-// The arrival word is (tag << 32) | count with a tag unique to the launch:
-// a word holding any other tag (stale words of earlier launches, partial
-// sums of other shapes, uninitialized memory) counts as zero, so the
-// workspace needs no initialization.  The arrival words follow the partials
-// at a 256-byte aligned offset (in floats):
+// The arrival word is (tag << 32) | count with a tag unique to the launch
+// (never 0): a word holding any other tag (stale words of earlier launches,
+// partial sums of other shapes, uninitialized memory) counts as zero, so the
+// workspace needs no initialization.  The last arrival writes 0 instead of
+// the full count, so a launch replayed with the same tag (a captured HIP
+// graph bakes the tag into the kernel arguments) finds the word at zero
+// again.  The arrival words follow the partials at a 256-byte aligned
+// offset (in floats):
 __host__ __device__ inline size_t split_counter_floats(int S, int M, int N) {
     return ((size_t)S * (size_t)M * (size_t)N + 63) / 64 * 64;
 }
@@ -242,15 +245,18 @@ __device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t pl, const f
     }
 }
 
-// Count one arrival at word w; true for the S-th arrival of this launch.
+// Count one arrival at word w; true for the S-th arrival of this launch,
+// which leaves the word at 0 (no other workgroup of the launch touches it
+// after that).
 __device__ __forceinline__ bool split_arrive(unsigned long long* w, uint32_t tag, int S) {
     unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (;;) {  // each failed exchange is another workgroup's arrival: at most S - 1 retries
         const uint32_t cnt = (uint32_t)(old >> 32) == tag ? (uint32_t)old : 0u;
-        const unsigned long long nw = ((unsigned long long)tag << 32) | (unsigned long long)(cnt + 1);
+        const bool last = cnt + 1 == (uint32_t)S;
+        const unsigned long long nw = last ? 0ull : ((unsigned long long)tag << 32) | (unsigned long long)(cnt + 1);
         if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT))
-            return cnt + 1 == (uint32_t)S;
+            return last;
     }
 }
 
@@ -962,11 +968,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
 //   NVFP4: scale byte = E4M3 round-to-nearest-even of (amax / 6) / alpha,
 //          saturated at 448, at least 2^-9 (byte 1);
 //   MXFP4: scale byte = clamp(floor(log2(amax / alpha)) - 2 + 127, 0, 254),
-//          255 never; byte 0 marks a zero block (all codes 0);
+//          255 never; byte 0 is the scale 2^-127 (an FP32 subnormal) and
+//          its block is rounded like any other;
 //   S = alpha * scale, q = |x| / S, code = nearest E2M1 value to q with
 //   ties to the even mantissa bit, saturating at 6; the sign bit only on
-//   non-zero codes.  NaN elements give 0 (amax ignores them); infinities
-//   give +-6 and the largest scale.
+//   non-zero codes.  Zero and NaN elements give code 0 (amax ignores NaN);
+//   infinities give the largest scale.
 // One thread per block of G elements: the blocks of a row are consecutive
 // in memory, so a wave reads and writes contiguous bytes.
 
@@ -1024,7 +1031,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     for (int i = 0; i < G; ++i) amax = fmaxf(amax, fabsf(x[i]));  // fmaxf drops NaN operands
     uint32_t sb;
     float sval;
-    bool zero_block = false;
     if constexpr (FMT == 0) {
         sb = e4m3_rne(__fdiv_rn(__fdiv_rn(amax, 6.0f), alpha));
         sb = sb == 0 ? 1u : sb;
@@ -1033,8 +1039,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
         const float t = __fdiv_rn(amax, alpha);
         const int ef = int((__float_as_uint(t) >> 23) & 0xFF);  // 0: zero or below 2^-126; 255: infinite
         sb = ef == 255 ? 254u : (uint32_t)max(ef - 2, 0);
-        zero_block = sb == 0;
-        sval = __uint_as_float(sb << 23);  // 2^(sb - 127) for sb >= 1
+        // 2^(sb - 127); byte 0 is 2^-127, the FP32 subnormal 0x00400000
+        sval = __uint_as_float(sb != 0 ? sb << 23 : 0x00400000u);
     }
     const float S = __fmul_rn(alpha, sval);
     uint32_t out[G / 8];
@@ -1045,7 +1051,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     // (at most 3 significant bits) as |x| does of c x S, which is exact in
     // FP32: a quotient that is not c differs from it by at least 2^-8 / 300
     // relative, far more than the half-ulp the division rounds by.  Then the
-    // decision needs no division (S below 2^120 keeps 5 S finite).
+    // decision needs no division (S below 2^120 keeps 5 S finite; S of a
+    // block with a non-zero element is at least about amax / 8 >= 2^-136,
+    // so every threshold c x S is an exact FP32 value, subnormals included;
+    // only an all-zero block's S can underflow to 0, and zero elements get
+    // code 0 below whatever the thresholds are).
     const bool exact_thresholds = (__float_as_uint(alpha) & 0x007FFFFFu) == 0u && S < 0x1p120f;
     const float t0 = 0.25f * S, t1 = 0.75f * S, t2 = 1.25f * S, t3 = 1.75f * S, t4 = 2.5f * S, t5 = 3.5f * S,
                 t6 = 5.0f * S;
@@ -1061,7 +1071,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
             c = (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) + (uint32_t)(q >= 1.75f) +
                 (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) + (uint32_t)(q > 5.0f);
         }
-        if (zero_block) c = 0;
+        if (!(ax > 0.0f)) c = 0;  // zero or NaN (q = 0 or NaN)
         if (c != 0 && x[i] < 0.0f) c |= 8u;
         out[i / 8] |= c << (4 * (i % 8));
     }

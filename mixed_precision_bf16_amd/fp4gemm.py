@@ -289,10 +289,9 @@ def native_repack(codes, scales, N: int, K: int):
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     if codes.size != N * K // 2 or scales.size != N * (K // 32):
         raise ValueError("codes / scales have the wrong size")
-    wqb, sqb = _c_sz(), _c_sz()
-    _check(lib().fp4_native_repack_size(N, K, ctypes.byref(wqb), ctypes.byref(sqb)), "fp4_native_repack_size")
-    wq = np.empty(wqb.value, np.uint8)
-    sq = np.empty(sqb.value, np.uint8)
+    nw, ns = native_repack_size(N, K)
+    wq = np.empty(nw, np.uint8)
+    sq = np.empty(ns, np.uint8)
     _check(lib().fp4_native_repack(codes.ctypes.data_as(_c_vp), scales.ctypes.data_as(_c_vp), N, K,
                                    wq.ctypes.data_as(_c_vp), sq.ctypes.data_as(_c_vp)), "fp4_native_repack")
     return torch.from_numpy(wq), torch.from_numpy(sq)
@@ -316,20 +315,36 @@ def native_workspace_size(m: int, N: int, K: int) -> int:
     return b.value
 
 
+def native_repack_size(N: int, K: int):
+    wqb, sqb = _c_sz(), _c_sz()
+    _check(lib().fp4_native_repack_size(N, K, ctypes.byref(wqb), ctypes.byref(sqb)), "fp4_native_repack_size")
+    return wqb.value, sqb.value
+
+
 def gemm_native(A, wq, sq, N: int, K: int, out=None, workspace=None, stream=None, alpha: float = 1.0):
     """fp4_gemm_native: C = alpha * dequant(quantize_mxfp4(A)) . dequant(W)^T
-    with W in the native layout; A bfloat16 CUDA [m][K]."""
+    with W in the native layout; A bfloat16 CUDA [m][K]; wq / sq uint8 CUDA
+    tensors of native_repack_size(N, K) bytes (upload native_repack's CPU
+    tensors first)."""
     import torch
     if A.dtype != torch.bfloat16 or A.dim() != 2 or not A.is_cuda or not A.is_contiguous() or A.shape[1] != K:
         raise ValueError("A must be a contiguous bfloat16 CUDA tensor [m][K]")
+    nw, ns = native_repack_size(N, K)
+    for t, n in ((wq, nw), (sq, ns)):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
+            raise ValueError("wq / sq must be contiguous uint8 CUDA tensors of native_repack_size(N, K) bytes")
     m = A.shape[0]
     if out is None:
         out = torch.empty((m, N), dtype=torch.bfloat16, device=A.device)
+    elif out.shape != (m, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor [m][N]")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
+    _on_device_of(A, wq=wq, sq=sq, out=out, workspace=workspace)
     need = native_workspace_size(m, N, K)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
-    ws_bytes = workspace.numel() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().fp4_gemm_native(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), m, N, K, alpha,
                                  _dev_ptr(workspace), ws_bytes, _stream_handle(stream)), "fp4_gemm_native")
     return out
-

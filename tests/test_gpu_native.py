@@ -114,3 +114,28 @@ def test_native_repeat_bit_identical():
     _say("native determinism")
     a, b = run_native(p, reps=2)
     assert np.array_equal(a, b)
+
+
+def test_native_binding_rejects_host_and_misshaped_tensors():
+    # native_repack returns CPU tensors: handing them on unuploaded would give
+    # the kernel host pointers, so the binding refuses them before any launch
+    p = synth.make_random(16, 64, 512, 1, seed=23)
+    wq, sq = F.native_repack(p.codes, p.scales, p.N, p.K)
+    A = torch.from_numpy(p.a_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    _say("native binding checks")
+    with pytest.raises(ValueError):
+        F.gemm_native(A, wq, sq, p.N, p.K)
+    wq_d, sq_d = wq.cuda(), sq.cuda()
+    with pytest.raises(ValueError):
+        F.gemm_native(A, wq_d, sq, p.N, p.K)
+    with pytest.raises(ValueError):
+        F.gemm_native(A, wq_d[:-16], sq_d, p.N, p.K)
+    with pytest.raises(ValueError):
+        F.gemm_native(A, wq_d, sq_d, p.N, p.K, out=torch.empty((16, 64), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        F.gemm_native(A, wq_d, sq_d, p.N, p.K, out=torch.empty((16, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        F.gemm_native(A, wq_d, sq_d, p.N, p.K, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    y = F.gemm_native(A, wq_d, sq_d, p.N, p.K)   # the valid call still works
+    torch.cuda.synchronize()
+    check(p, _bits(y))

@@ -129,3 +129,65 @@ def test_gemm_ex_alpha(m, N, K, fmt, act):
     y_ref, bound = oracle.gemm_reference(p.a_bits, p.codes[rows], p.scales[rows], K, fmt, p.act)
     y_ref, bound = oracle.scaled_gemm_reference(y_ref, bound, 0.3)
     assert oracle.check_tolerance(yb[:, rows], y_ref, bound, act=p.act).all()
+
+
+def tiny_mx_weights(N, seed):
+    """BF16 weight bits [N][128] whose MXFP4 blocks have maxima below 2^-124
+    (scale byte 0 = 2^-127, the FP32 subnormal on the device) or just above
+    it, plus exact code x 2^-127 / 2^-126 / 2^-125 blocks (the fixed point of
+    the quantizer at scale bytes 0, 1, 2) and the smallest BF16 subnormal."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    amax = np.array([2.0 ** -126, 1.5 * 2.0 ** -125, 1.8984375 * 2.0 ** -125, 2.0 ** -124, 1.75 * 2.0 ** -127,
+                     2.0 ** -123])
+    w = np.zeros((N, 128), np.float32)
+    for i in range(N):
+        for b in range(4):
+            a = amax[(i + b) % len(amax)]
+            blk = (rng.uniform(-1, 1, size=32) * a).astype(np.float32)
+            blk[rng.integers(0, 32)] = a if (i + b) % 2 == 0 else -a
+            blk[rng.integers(0, 32)] = 2.0 ** -133
+            w[i, 32 * b:32 * b + 32] = blk
+    ex = rng.integers(0, 16, size=(3, 128))
+    ex[ex == 8] = 0
+    ex[:, ::32] = 7
+    vals = oracle.e2m1_value(ex) * np.exp2(np.array([-127.0, -126.0, -125.0]))[:, None]
+    w[:3] = vals.astype(np.float32)
+    return torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("alpha", [1.0, 2.0 ** -7, 0.37, 8.0])
+def test_quantize_tiny_mxfp4_blocks_bit_exact(alpha):
+    """Scale byte 0 is the scale 2^-127 and its block is rounded like any
+    other (block scaling: divide by the block's scale, then round)."""
+    bits = tiny_mx_weights(24, seed=77)
+    _say("quantize tiny mxfp4", alpha)
+    want_c, want_s = oracle.quantize_reference(bits, 1, alpha)
+    if alpha == 1.0:
+        assert np.any(want_s == 0) and np.any(want_c[want_s.repeat(16, axis=1) == 0] != 0)
+    W = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    c, s = F.quantize(W, 1, alpha)
+    torch.cuda.synchronize()
+    c, s = c.cpu().numpy(), s.cpu().numpy()
+    assert np.array_equal(s, want_s), np.argwhere(s != want_s)[:5]
+    assert np.array_equal(c, want_c), np.argwhere(c != want_c)[:5]
+
+
+def test_native_tiny_activation_blocks():
+    """The native path quantizes its activations with the same rule: rows of
+    A made of blocks below 2^-124 (scale byte 0) against MXFP4 weights with
+    large scales (2^30 .. 2^40, so the products stay FP32 normals) meet
+    oracle.native_reference."""
+    m, N, K = 24, 96, 128
+    a_bits = tiny_mx_weights(m, seed=78)
+    p = synth.make_random(m, N, K, 1, seed=79, scale_lo=30, scale_hi=40)
+    p = synth.Problem("native_tiny", m, N, K, 1, a_bits, p.codes, p.scales, 79)
+    _say("native tiny activations")
+    wq, sq = F.native_repack(p.codes, p.scales, N, K)
+    A = torch.from_numpy(a_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    y = F.gemm_native(A, wq.cuda(), sq.cuda(), N, K)
+    torch.cuda.synchronize()
+    yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    y_ref, bound = oracle.native_reference(a_bits, p.codes, p.scales, K)
+    assert np.all(np.abs(y_ref).max(axis=1) > 0), "every row keeps non-zero quantized activations"
+    assert oracle.check_tolerance(yb, y_ref, bound).all()
+

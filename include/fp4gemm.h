@@ -143,6 +143,27 @@ int fp4_gemm(const void* A, const void* wq, const void* sq, void* C,
              int64_t m, int64_t N, int64_t K, int format,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/* fp4_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and results (bit for bit) as fp4_gemm, without
+ * workspace arguments.  The split-K scratch (fp4_gemm_workspace_size bytes)
+ * lives in a 64 MiB device array of the library instead, one per GPU the
+ * library runs on, held until the process ends; problems whose workspace
+ * size exceeds fp4_gemm_noalloc_max_workspace() return FP4_ERR_WORKSPACE
+ * (checked before any HIP call).  The call allocates and frees nothing.
+ * All calls on one GPU share its array: calls that overlap in time on one
+ * GPU (several streams or threads at once) race and give wrong results;
+ * serialize them.  The array keeps the last call's contents; nothing in it
+ * needs clearing between calls (the split-K arrival words carry launch tags
+ * and are left at zero).  The first call on each device looks the array's
+ * address up (hipGetSymbolAddress); make that first call outside a graph
+ * capture.  Other arguments, errors and determinism as fp4_gemm. */
+int fp4_gemm_noalloc(const void* A, const void* wq, const void* sq, void* C,
+                     int64_t m, int64_t N, int64_t K, int format, void* stream);
+
+/* Size in bytes of fp4_gemm_noalloc's per-GPU scratch array (64 MiB). */
+size_t fp4_gemm_noalloc_max_workspace(void);
+
 /* Same as fp4_gemm with FP16 activations and output: A device FP16 [m][K],
  * C device FP16 [m][N] (the Petit blog, "Introduction": FP16/BF16 x FP4
  * kernels).  The weights use the same packed layout; they are dequantized

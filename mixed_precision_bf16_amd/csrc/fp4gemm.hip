@@ -319,8 +319,37 @@ static bool alpha_ok(float alpha) {
     return a == 1.0f || (a >= 0x1p-100f && a <= 0x1p100f);
 }
 
+// Scratch of fp4_gemm_noalloc: the split-K partial sums and arrival words
+// that fp4_gemm keeps in the caller's workspace, in a file-scope device
+// array instead.  Every GPU the library runs on holds its own copy until the
+// process ends; host code never uses the array's name as an address, only
+// the per-device pointer hipGetSymbolAddress returns for it.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];  // per device id, set once with that device current
+
+// The current device's address of `scratch` (looked up on the first call on
+// each device).
+static int noalloc_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FP4_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FP4_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FP4_OK;
+}
+
+// use_scratch: fp4_gemm_noalloc (workspace arguments ignored; the device's
+// `scratch` array serves as the workspace, FP4_ERR_WORKSPACE beyond its size).
 static int gemm_impl(int act, const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N,
-                     int64_t K, int format, float alpha, void* workspace, size_t workspace_bytes, void* stream) {
+                     int64_t K, int format, float alpha, void* workspace, size_t workspace_bytes, void* stream,
+                     bool use_scratch = false) {
     int st = fp4_check_weight_shape(N, K, format);
     if (st != FP4_OK) return st;
     if (act != 0 && act != 1) return FP4_ERR_FORMAT;
@@ -334,10 +363,18 @@ static int gemm_impl(int act, const void* A, const void* wq, const void* sq, voi
     if (round_up(m, a_row_block(m)) * K * 2 >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
     const GemmPlan plan = cached_plan(format, m, N, K);
     const size_t need = plan.ws_bytes;
-    if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15)))
+    if (use_scratch) {
+        if (need > kNoAllocScratchBytes) return FP4_ERR_WORKSPACE;
+    } else if (need > 0 &&
+               (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15))) {
         return FP4_ERR_WORKSPACE;
+    }
     st = check_device();
     if (st != FP4_OK) return st;
+    if (use_scratch && need > 0) {
+        st = noalloc_scratch(&workspace);
+        if (st != FP4_OK) return st;
+    }
     const int64_t Np = padded_n(N), Kp = padded_k(K);
     const int KB = int(Kp / kChunkK), SB = int(Kp / kScaleBlockK), NT = int(Np / kTileN);
     (void)hipGetLastError();
@@ -567,6 +604,13 @@ extern "C" int fp4_gemm(const void* A, const void* wq, const void* sq, void* C, 
                         int format, void* workspace, size_t workspace_bytes, void* stream) {
     return gemm_impl(0, A, wq, sq, C, m, N, K, format, 1.0f, workspace, workspace_bytes, stream);
 }
+
+extern "C" int fp4_gemm_noalloc(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N,
+                                int64_t K, int format, void* stream) {
+    return gemm_impl(0, A, wq, sq, C, m, N, K, format, 1.0f, nullptr, 0, stream, true);
+}
+
+extern "C" size_t fp4_gemm_noalloc_max_workspace(void) { return kNoAllocScratchBytes; }
 
 extern "C" int fp4_gemm_f16(const void* A, const void* wq, const void* sq, void* C, int64_t m, int64_t N, int64_t K,
                             int format, void* workspace, size_t workspace_bytes, void* stream) {

@@ -33,6 +33,8 @@ _SIGNATURES = {
     "fp4_gemm_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.POINTER(_c_sz)]),
     "fp4_gemm": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_vp, _c_sz,
                                 _c_vp]),
+    "fp4_gemm_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
+    "fp4_gemm_noalloc_max_workspace": (ctypes.c_size_t, []),
     "fp4_gemm_f16": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_vp,
                                     _c_sz, _c_vp]),
     "fp4_dequant": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_int, _c_vp]),
@@ -201,6 +203,28 @@ def gemm(A, wq, sq, N: int, K: int, fmt: int, out=None, workspace=None, stream=N
     fn = lib().fp4_gemm if A.dtype == torch.bfloat16 else lib().fp4_gemm_f16
     _check(fn(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), m, N, K, fmt, _dev_ptr(workspace), ws_bytes,
               _stream_handle(stream)), "fp4_gemm")
+    return out
+
+
+def gemm_noalloc(A, wq, sq, N: int, K: int, fmt: int, out, stream=None):
+    """fp4_gemm_noalloc: Y = A . dequant(W)^T with the library's own per-GPU
+    scratch instead of a workspace (nothing is allocated; `out`, a contiguous
+    bfloat16 CUDA tensor [m][N], must be given)."""
+    import torch
+    if A.dtype != torch.bfloat16 or A.dim() != 2 or not A.is_cuda or not A.is_contiguous() or A.shape[1] != K:
+        raise ValueError("A must be a contiguous bfloat16 CUDA tensor [m][K]")
+    for t in (wq, sq):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("wq / sq must be contiguous uint8 CUDA tensors")
+    nw, ns = repack_size(N, K, fmt)
+    if wq.numel() != nw or sq.numel() != ns:
+        raise ValueError("packed weight tensors have the wrong size")
+    m = A.shape[0]
+    if out is None or out.shape != (m, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor [m][N]")
+    _on_device_of(A, wq=wq, sq=sq, out=out)
+    _check(lib().fp4_gemm_noalloc(_dev_ptr(A), _dev_ptr(wq), _dev_ptr(sq), _dev_ptr(out), m, N, K, fmt,
+                                  _stream_handle(stream)), "fp4_gemm_noalloc")
     return out
 
 

@@ -321,3 +321,17 @@ def test_gemm_rejects_small_or_misaligned_workspace_before_any_hip_call():
     assert lib.fp4_gemm(d, d, d, d, m, N, K, 0, ctypes.c_void_p((1 << 20) + 4), need, None) == 5
     # misaligned operands
     assert lib.fp4_gemm(ctypes.c_void_p((1 << 20) + 2), d, d, d, m, N, K, 0, d, need, None) == 2
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    # fp4_gemm_noalloc checks the workspace the problem needs against its
+    # 64 MiB per-GPU scratch array before any HIP call
+    lib = F.lib()
+    assert lib.fp4_gemm_noalloc_max_workspace() == 64 << 20
+    m, N, K, fmt = 640, 57344, 262144, 0
+    assert F.workspace_size(m, N, K, fmt) > lib.fp4_gemm_noalloc_max_workspace()
+    d = ctypes.c_void_p(256)   # never dereferenced
+    assert lib.fp4_gemm_noalloc(d, d, d, d, m, N, K, fmt, None) == 5      # FP4_ERR_WORKSPACE
+    assert lib.fp4_gemm_noalloc(d, d, d, d, 16, 64, 100, 0, None) == 2    # K % 16 != 0
+    assert lib.fp4_gemm_noalloc(None, d, d, d, 16, 64, 512, 0, None) == 1
+    assert lib.fp4_gemm_noalloc(d, d, d, d, 0, 64, 512, 0, None) == 0     # m == 0: no-op

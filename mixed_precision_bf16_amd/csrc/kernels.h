@@ -247,16 +247,28 @@ __device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t pl, const f
 
 // Count one arrival at word w; true for the S-th arrival of this launch,
 // which leaves the word at 0 (no other workgroup of the launch touches it
-// after that).
+// after that).  A word that already carries this launch's tag is counted
+// with one atomic add (its count is below S, so no reset can intervene and
+// the add never carries into the tag); a word with another tag is claimed
+// with a compare-exchange that installs (tag, 1).  Workgroups that arrive
+// together thus pay at most one failed exchange each, then one add, instead
+// of retrying an exchange once per earlier arrival.
 __device__ __forceinline__ bool split_arrive(unsigned long long* w, uint32_t tag, int S) {
-    unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (;;) {  // each failed exchange is another workgroup's arrival: at most S - 1 retries
-        const uint32_t cnt = (uint32_t)(old >> 32) == tag ? (uint32_t)old : 0u;
-        const bool last = cnt + 1 == (uint32_t)S;
-        const unsigned long long nw = last ? 0ull : ((unsigned long long)tag << 32) | (unsigned long long)(cnt + 1);
-        if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT))
-            return last;
+    const unsigned long long mine = (unsigned long long)tag << 32;
+    unsigned long long cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {  // a failed exchange means another workgroup changed the word: at most S - 1 turns
+        uint32_t cnt;
+        if ((cur >> 32) == (unsigned long long)tag) {
+            cnt = (uint32_t)__hip_atomic_fetch_add(w, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        } else if (__hip_atomic_compare_exchange_strong(w, &cur, S == 1 ? 0ull : mine | 1ull, __ATOMIC_RELAXED,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            cnt = 1u;
+        } else {
+            continue;  // cur now holds the word's value
+        }
+        if (cnt == (uint32_t)S && S > 1)
+            __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return cnt == (uint32_t)S;
     }
 }
 

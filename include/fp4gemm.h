@@ -288,8 +288,8 @@ int fp4_gemm_native(const void* A, const void* wq, const void* sq, void* C, int6
  * A, wq, sq and C 16-byte aligned, the int32 / FP32 arrays 4-byte aligned.
  * P == 0 is a no-op.  No workspace (no K split).  Asynchronous on `stream`;
  * deterministic.  Errors as for fp4_gemm; FP4_ERR_SHAPE also for E outside
- * 1 .. 4096, P > 2^24, a_div < 1 or a grid that would need more than 65535
- * row blocks (P / 16 + E). */
+ * 1 .. 4096, P > 2^24, a_div < 1, out_rows * N * 2 bytes of C at or above
+ * 2^31, or a grid that would need more than 65535 row blocks (P / 16 + E). */
 int fp4_moe_gemm(const void* A, const void* wq, const void* sq, const int32_t* sorted_ids,
                  const int32_t* expert_offsets, const float* topk_weights, void* C, int64_t a_rows, int64_t a_div,
                  int64_t out_rows, int64_t P, int64_t E, int64_t N, int64_t K, int format, void* stream);

@@ -186,7 +186,9 @@ static bool prefill_compiled(const PrefillShape& t) {
 // n-tiles, so each dequantized fragment feeds 8 products and one wave's
 // vector work overlaps the other's matrix work (about 10 % faster than four
 // waves of four n-tiles); the K split S minimizes the rounds of workgroups
-// per unit of work (QKV 3, O and down 4, gate_up 1 at m = 256).
+// per unit of work (QKV 3, O and down 4, gate_up 1 at m = 256).  128 x 128
+// tiles with a smaller split measured faster on down on one box (121 against
+// 128 us) and slower on another (142 against 127 us), so they are not picked.
 // FP4GEMM_PREFILL="WM,WN,MBW,TNW,S" overrides it.
 static PrefillShape pick_prefill(int fmt, int64_t M, int64_t N, int NT, int SB) {
     (void)fmt;
@@ -361,6 +363,7 @@ static int gemm_impl(int act, const void* A, const void* wq, const void* sq, voi
          reinterpret_cast<uintptr_t>(C)) & 15)
         return FP4_ERR_SHAPE;
     if (round_up(m, a_row_block(m)) * K * 2 >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
+    if (m * N * 2 >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;  // Y through 32-bit ranged offsets
     const GemmPlan plan = cached_plan(format, m, N, K);
     const size_t need = plan.ws_bytes;
     if (use_scratch) {
@@ -431,6 +434,7 @@ static int moe_impl(const void* A, const void* wq, const void* sq, const int32_t
          reinterpret_cast<uintptr_t>(topw)) & 3)
         return FP4_ERR_SHAPE;
     if (round_up(a_rows, 64) * K * 2 >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
+    if (out_rows * N * 2 >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;  // C through 32-bit ranged offsets
     const int64_t Np = padded_n(N), Kp = padded_k(K);
     const int KB = int(Kp / kChunkK), SB = int(Kp / kScaleBlockK), NT = int(Np / kTileN);
     const int64_t G = format == FP4_NVFP4 ? 16 : 32;
@@ -507,7 +511,7 @@ static NativePlan native_plan(int64_t m, int64_t N, int64_t K) {
     p.partial_off = round_up(p.scales_off + p.scales_bytes, 256);
     const int64_t blocks = ((m + native_bm() - 1) / native_bm()) * ((NT + native_bnt() - 1) / native_bnt());
     p.S = 1;
-    while (p.S < 8 && 2 * p.S <= QB && blocks * 2 * p.S <= kCUs) p.S *= 2;
+    while (p.S < 8 && 2 * p.S <= QB && blocks * 2 * p.S <= kCUs && m * N < (int64_t(1) << 29)) p.S *= 2;
     p.total = size_t(p.partial_off) + (p.S > 1 ? size_t(p.S) * size_t(m) * size_t(N) * 4 : 0);
     return p;
 }

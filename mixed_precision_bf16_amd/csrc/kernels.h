@@ -179,27 +179,32 @@ __device__ __forceinline__ uint32_t pack_out(float lo, float hi) {
     }
 }
 
-// Store one 16x16 output fragment: lane holds Y[m][n0 .. n0+3] (MFMA output
-// rows are n, columns are m).
-template <int ACT = 0>
-__device__ __forceinline__ void store_frag(uint16_t* __restrict__ C, const f32x4& v, int m, int n0, int M, int N) {
-    if (m >= M) return;
-    const uint32_t p0 = pack_out<ACT>(v.x, v.y), p1 = pack_out<ACT>(v.z, v.w);
-    uint16_t* dst = C + (size_t)m * N + n0;
-    if ((N & 3) == 0 && n0 + 3 < N) {
-        u32x2 pv = {p0, p1};
-        *reinterpret_cast<u32x2*>(dst) = pv;
-    } else {
-        const uint16_t h[4] = {(uint16_t)(p0 & 0xFFFF), (uint16_t)(p0 >> 16), (uint16_t)(p1 & 0xFFFF),
-                               (uint16_t)(p1 >> 16)};
-        for (int e = 0; e < 4; ++e)
-            if (n0 + e < N) dst[e] = h[e];
-    }
-}
-
-// ------------------------------------------------------------ buffer loads
+// ------------------------------------------------------------ buffer access
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufWord3);
+}
+
+// Store one 16x16 output fragment: lane holds Y[m][n0 .. n0+3] (MFMA output
+// rows are n, columns are m) of the [M][N] output (M * N * 2 < 2^31 bytes).
+// Ranged buffer stores: an element at or past row M or column N gets an
+// offset past the buffer's range and the hardware drops it, so the epilogue
+// has no branches (the Petit blog, "Generating high-quality machine code":
+// ranged memory instructions discard out-of-bounds accesses).
+template <int ACT = 0>
+__device__ __forceinline__ void store_frag(uint16_t* __restrict__ C, const f32x4& v, int m, int n0, int M, int N) {
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, (uint32_t)M * (uint32_t)N * 2u);
+    const uint32_t p0 = pack_out<ACT>(v.x, v.y), p1 = pack_out<ACT>(v.z, v.w);
+    const uint32_t base = ((uint32_t)m * (uint32_t)N + (uint32_t)n0) * 2u;  // used only when in range
+    if ((N & 3) == 0) {  // the four columns are all inside or all past N
+        const uint32_t off = (m < M && n0 < N) ? base : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{p0, p1}, rc, off, 0, 0);
+    } else {
+        const uint32_t h[4] = {p0 & 0xFFFFu, p0 >> 16, p1 & 0xFFFFu, p1 >> 16};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h[e], rc,
+                                                  (m < M && n0 + e < N) ? base + 2u * e : kOutOfRange, 0, 0);
+    }
 }
 
 template <int FMT>
@@ -233,15 +238,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t split_plane(const float* P, in
 }
 
 // Store the FP32 partials of one 16x16 output fragment (lane: row m, columns
-// n0 .. n0 + 3) into plane `pl`; columns at or past N are dropped.
-__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t pl, const f32x4& v, int m, int n0, int N) {
-    const uint32_t off = (uint32_t)(m * N + n0) * 4u;
-    if ((N & 3) == 0 && n0 + 3 < N) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), pl, off, 0, kDeviceCoherent);
+// n0 .. n0 + 3) into plane `pl` with device-coherent ranged stores; rows at
+// or past M and columns at or past N are dropped.
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t pl, const f32x4& v, int m, int n0, int M,
+                                              int N) {
+    const uint32_t off = ((uint32_t)m * (uint32_t)N + (uint32_t)n0) * 4u;  // used only when in range
+    if ((N & 3) == 0) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), pl,
+                                               (m < M && n0 < N) ? off : kOutOfRange, 0, kDeviceCoherent);
     } else {
+#pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (n0 + e < N) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), pl, off + 4 * e, 0,
-                                                                  kDeviceCoherent);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), pl,
+                                                  (m < M && n0 + e < N) ? off + 4 * e : kOutOfRange, 0,
+                                                  kDeviceCoherent);
     }
 }
 
@@ -672,7 +682,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void gemm_decode(const uint16_t* __
         for (int tt = 0; tt < TN; ++tt)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
-                if (mb * 16 + r < M) store_partial(pl, acc[tt][mb], mb * 16 + r, (tile0 + tt) * kTileN + 4 * j, N);
+                store_partial(pl, acc[tt][mb], mb * 16 + r, (tile0 + tt) * kTileN + 4 * j, M, N);
     }
     const int n_begin = grp * (TN * NWN) * kTileN;
     split_finish<ACT, 64 * NWN * NWK>(P, C, M, N, S, grp, 0, M, n_begin, min(N, n_begin + TN * NWN * kTileN), alpha,
@@ -958,7 +968,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
             const int m = m0 + wm * MBW * 16 + mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
             if (P == nullptr) {
                 store_frag<ACT>(C, acc[tt][mb] * alpha, m, n0, M, N);
-            } else if (m < M) {
+            } else if (m < M) {  // FP32 partials for the reduce kernel (plain stores: measured faster here)
                 float* dst = P + ((size_t)ks * M + m) * N + n0;
                 if ((N & 3) == 0 && n0 + 3 < N) {
                     *reinterpret_cast<f32x4*>(dst) = acc[tt][mb];
@@ -1270,7 +1280,7 @@ __global__ __launch_bounds__(256) void gemm_native(const uint8_t* __restrict__ A
             const int m = m0 + wm * MBW * 16 + mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
             if (P == nullptr) {
                 store_frag<0>(C, acc[tt][mb] * alpha, m, n0, M, N);
-            } else if (m < M) {
+            } else if (m < M) {  // FP32 partials for the reduce kernel (plain stores: measured faster here)
                 float* dst = P + ((size_t)ks * M + m) * N + n0;
                 if ((N & 3) == 0 && n0 + 3 < N) {
                     *reinterpret_cast<f32x4*>(dst) = acc[tt][mb];

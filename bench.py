@@ -66,12 +66,106 @@ def measured_traffic():
     when the kernel sources changed since the counters were taken."""
     try:
         rec = json.load(open(TRAFFIC_RECORD))
-        h = hashlib.sha256()
-        for f in rec["sources"]:
-            h.update(open(os.path.join(ROOT, f), "rb").read())
-        return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+        return rec["hbm_bytes_per_launch"] if sources_sha256(rec["sources"]) == rec["source_sha256"] else None
     except (OSError, KeyError, ValueError):
         return None
+
+
+KERNEL_SOURCES = ["mixed_precision_bf16_amd/csrc/kernels.h", "mixed_precision_bf16_amd/csrc/layout.h",
+                  "mixed_precision_bf16_amd/csrc/dispatch.h", "mixed_precision_bf16_amd/csrc/decode_inst.inc",
+                  "mixed_precision_bf16_amd/csrc/decode_bf16.hip", "mixed_precision_bf16_amd/csrc/prefill_inst.inc",
+                  "mixed_precision_bf16_amd/csrc/prefill_bf16.hip", "mixed_precision_bf16_amd/csrc/fp4gemm.hip"]
+COUNTER_RECORD = os.path.join(ROOT, "profiles", "counters_gemm_prefill_decode_nvfp4.json")
+GATE_UP_DECODE_KERNEL = "gemm_decode<0, 0, 1, 2, 7, 2, false>"
+
+
+def sources_sha256(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    (path,) = glob.glob(os.path.join(d, "*_counter_collection.csv"))
+    return list(csv.DictReader(open(path)))
+
+
+def traffic_record(fetch_dir, write_dir):
+    """FETCH_SIZE and WRITE_SIZE passes (rocprofv3 --pmc, one counter per run,
+    each run starting with the 256 MiB calibration copy of --calibrate-copy)
+    -> the HBM bytes per gate/up decode launch, each counter scaled by what it
+    reads for the copy of known size; written to TRAFFIC_RECORD with the
+    SHA-256 of the kernel sources."""
+    import statistics
+    out = {}
+    for d, name in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
+        copy = [float(r["Counter_Value"]) for r in rows if "__amd_rocclr_copyBuffer" in r["Kernel_Name"]]
+        gu = [float(r["Counter_Value"]) for r in rows if GATE_UP_DECODE_KERNEL in r["Kernel_Name"]]
+        out[name] = (copy[0], statistics.mean(gu), len(gu))
+    cb = 256 << 20
+    ff, wf = cb / (out["FETCH_SIZE"][0] * 1024), cb / (out["WRITE_SIZE"][0] * 1024)
+    hbm = int(round(out["FETCH_SIZE"][1] * 1024 * ff + out["WRITE_SIZE"][1] * 1024 * wf))
+    rec = {"kernel": "gemm_decode<0,0,1,2,7,2> (gate_up 57344x8192, m=16, NVFP4, BF16 activations)",
+           "sources": KERNEL_SOURCES, "source_sha256": sources_sha256(KERNEL_SOURCES),
+           "command": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d <fetch> -o f -- "
+                      "python3 <repo>/bench.py --calibrate-copy --steps 3 --warmup 1 --no-prefill --no-cpu-baseline "
+                      "--no-fp16 --no-moe --no-quantize --no-blas --no-configs  (then the same with --pmc WRITE_SIZE "
+                      "into <write>); python3 bench.py --traffic-record <fetch> <write>",
+           "calibration": {"copy_bytes": cb, "copy_fetch_kib": out["FETCH_SIZE"][0],
+                           "copy_write_kib": out["WRITE_SIZE"][0], "fetch_factor": round(ff, 6),
+                           "write_factor": round(wf, 6)},
+           "fetch_kib_per_dispatch_mean": round(out["FETCH_SIZE"][1], 2),
+           "write_kib_per_dispatch_mean": round(out["WRITE_SIZE"][1], 2),
+           "dispatches": out["FETCH_SIZE"][2], "hbm_bytes_per_launch": hbm,
+           "algorithmic_bytes_per_launch": algorithmic_bytes(16, 57344, 8192, 16)}
+    json.dump(rec, open(TRAFFIC_RECORD, "w"), indent=1)
+    open(TRAFFIC_RECORD, "a").write("\n")
+    return rec
+
+
+def counter_record(pmc_dir):
+    """One SQ counter pass (rocprofv3 --pmc ... --kernel-trace) -> per kernel
+    instantiation and grid (one row per layer) the means per dispatch of every
+    counter and of the duration; written to COUNTER_RECORD with the SHA-256 of
+    the kernel sources."""
+    import csv
+    import glob
+    import statistics
+    rows = _counter_rows(pmc_dir)
+    (tpath,) = glob.glob(os.path.join(pmc_dir, "*_kernel_trace.csv"))
+    dur = {r["Dispatch_Id"]: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+           for r in csv.DictReader(open(tpath))}
+    per = {}  # dispatch -> (kernel, grid, {counter: value})
+    for r in rows:
+        if "fp4::" not in r["Kernel_Name"]:
+            continue
+        name = r["Kernel_Name"].split("(")[0].replace("void fp4::", "")
+        d = per.setdefault(r["Dispatch_Id"], (name, int(r["Grid_Size"]), {}))
+        d[2][r["Counter_Name"]] = float(r["Counter_Value"])
+    groups = {}  # one row per layer: kernel, grid and matrix-instruction count identify it
+    for i, (name, grid, cnt) in per.items():
+        groups.setdefault((name, grid, int(cnt.get("SQ_INSTS_MFMA", 0))), []).append(i)
+    table = []
+    for (name, grid, mfma), ids in sorted(groups.items()):
+        ent = {"kernel": name, "grid_threads": grid, "dispatches": len(ids),
+               "us_mean": round(statistics.mean(dur[i] for i in ids if i in dur), 2)}
+        for c in per[ids[0]][2]:
+            ent[c] = statistics.mean(per[i][2][c] for i in ids)
+        table.append(ent)
+    rec = {"sources": KERNEL_SOURCES, "source_sha256": sources_sha256(KERNEL_SOURCES),
+           "command": "cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU "
+                      "SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace "
+                      "--output-format csv -d <pmc> -o p -- python3 <repo>/bench.py --steps 3 --warmup 1 "
+                      "--no-cpu-baseline --no-fp16 --no-moe --no-quantize --no-blas --no-configs "
+                      "--prefill-launches 3; python3 bench.py --counter-record <pmc>",
+           "kernels": table}
+    json.dump(rec, open(COUNTER_RECORD, "w"), indent=1)
+    open(COUNTER_RECORD, "a").write("\n")
+    return rec
 
 
 def algorithmic_bytes(m, N, K, G):
@@ -96,6 +190,10 @@ def parse():
     ap.add_argument("--native", action="store_true", help="also time the native FP4 path (opt-in)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (known bytes for HBM counter scaling)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the gate/up traffic record from two rocprofv3 counter passes, then exit (no GPU)")
+    ap.add_argument("--counter-record", metavar="PMC_DIR",
+                    help="write the SQ counter record from a rocprofv3 counter pass, then exit (no GPU)")
     return ap.parse_args()
 
 
@@ -508,6 +606,14 @@ def moe_lines(args, F, torch, synth, dev):
 
 def main():
     args = parse()
+    if args.traffic_record:
+        rec = traffic_record(*args.traffic_record)
+        print(json.dumps({k: rec[k] for k in ("hbm_bytes_per_launch", "algorithmic_bytes_per_launch")}))
+        return
+    if args.counter_record:
+        rec = counter_record(args.counter_record)
+        print(f"{len(rec['kernels'])} kernel rows written to {COUNTER_RECORD}")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this GEMM has no multi-GPU path.",
               file=sys.stderr)

@@ -139,3 +139,39 @@ def test_native_binding_rejects_host_and_misshaped_tensors():
     y = F.gemm_native(A, wq_d, sq_d, p.N, p.K)   # the valid call still works
     torch.cuda.synchronize()
     check(p, _bits(y))
+
+
+def test_native_split_captured_in_a_graph_replays():
+    # activation quantizer + FP4 GEMM + reduce of a K split, captured once and
+    # replayed with new activations: every replay equals an eager call
+    m, N, K = 16, 1024, 8192
+    p = synth.make_random(m, N, K, 1, seed=31)
+    wq, sq = F.native_repack(p.codes, p.scales, N, K)
+    wq, sq = wq.cuda(), sq.cuda()
+    need = F.native_workspace_size(m, N, K)
+    _say("native graph replay", need)
+    A = torch.from_numpy(p.a_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty((m, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        F.gemm_native(A, wq, sq, N, K, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        F.gemm_native(A, wq, sq, N, K, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(13)
+    for rep in range(3):
+        A.copy_(torch.randn((m, K), generator=gen).to(torch.bfloat16).cuda())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = _bits(out)
+        want = _bits(F.gemm_native(A, wq, sq, N, K))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, want), f"replay {rep} differs from the eager call"
+    a_bits = A.view(torch.int16).cpu().numpy().view(np.uint16)
+    check(synth.Problem("native_graph", m, N, K, 1, a_bits, p.codes, p.scales, 31), got)

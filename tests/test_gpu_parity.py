@@ -471,3 +471,41 @@ def test_split_k_decode_captured_in_a_graph_replays(m, N, K, fmt):
         if rep in (0, 3):
             a_bits = a_rep.view(torch.int16).numpy().view(np.uint16)
             check_full(synth.Problem(f"graph_rep{rep}", m, N, K, fmt, a_bits, p.codes, p.scales, p.seed), got)
+
+
+@pytest.mark.parametrize("m,N,K,fmt,act", [(256, 8192, 2048, 0, "bf16"), (200, 520, 2560, 1, "f16")])
+def test_prefill_split_captured_in_a_graph_replays(m, N, K, fmt, act):
+    # a prefill GEMM with a K split (FP32 partials in the workspace, then the
+    # reduce kernel), captured once and replayed with new activations and
+    # eager work in between: every replay equals an eager call
+    need = F.workspace_size(m, N, K, fmt)
+    assert need > 0, "expected a K split"
+    _say("prefill graph replay", m, N, K, fmt, act)
+    p = synth.make_random(m, N, K, fmt, seed=600 + m + N + fmt, act=act)
+    wq, sq = F.upload(*F.repack(p.codes, p.scales, p.N, p.K, p.fmt))
+    gen = torch.Generator().manual_seed(12)
+    A = _to_dev_a(p.a_bits, act)
+    out = torch.empty((m, N), dtype=_tdt(act), device="cuda")
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=gen).cuda()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        F.gemm(A, wq, sq, N, K, fmt, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        F.gemm(A, wq, sq, N, K, fmt, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        a_rep = torch.randn((m, K), generator=gen).to(_tdt(act))
+        A.copy_(a_rep.cuda())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = _bits(out)
+        want = _bits(F.gemm(A, wq, sq, N, K, fmt))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, want), f"replay {rep} differs from the eager call"
+    a_bits = a_rep.view(torch.int16).numpy().view(np.uint16)
+    check_full(synth.Problem("pf_graph", m, N, K, fmt, a_bits, p.codes, p.scales, p.seed, act), got)

@@ -229,6 +229,27 @@ static bool wide_mid_m(int64_t M, int NT) {
     return M > 32 && M <= 64 && (NT + 15) / 16 >= 128;
 }
 
+// 33 <= m <= 64 on narrower layers: the prefill kernel with 64-row tiles
+// (eight waves of 4 m-blocks x 2 n-tiles) and a K split over one round of
+// workgroups, instead of the 64-row decode kernel, when the decode grid fills
+// the GPU poorly or K is long.  Measured on MI355X (m = 33 / 64, us, decode
+// kernel against 64-row prefill tiles): QKV 10240 x 8192 (decode grid 160 of
+// 256 CUs) 30.0 / 35.6 against 24.4 / 28.9 at S = 6; N = 8200, K = 8192 (130
+// CUs) 28.9 / 34.6 against 22.1 / 25.7; down 8192 x 28672 57.1 / 62.2
+// against 47.1 / 51.2 at S = 8; O 8192 x 8192 (256 CUs, K 8192) keeps the
+// decode kernel, 20.6 / 25.5 against 21.7 / 26.5.  Returns the split S (the
+// most workgroups that still fit one round, at most 8), or 0 for the decode
+// kernel.
+static int mid_m_prefill_split(const DecodeShape& d, int64_t K, int NT, int SB) {
+    const int64_t wgs = (int64_t)((NT + d.tn * d.nwn - 1) / (d.tn * d.nwn)) * d.s;
+    const int64_t rounds = (wgs + kCUs - 1) / kCUs;
+    if (4 * wgs >= 3 * rounds * kCUs && K <= 16384) return 0;
+    const int NG = (NT + 15) / 16;
+    int S = 1;
+    while (S < 8 && S < SB && (int64_t)NG * (S + 1) <= kCUs) ++S;
+    return S;
+}
+
 // The kernel, shape and K split chosen for one problem, and its workspace.
 struct GemmPlan {
     enum Kind { kDecode, kPrefill, kPrefillMid } kind;
@@ -250,6 +271,12 @@ static GemmPlan make_plan(int fmt, int64_t M, int64_t N, int64_t K) {
         p.MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
         p.d = pick_decode(fmt, p.MB, M, N, NT, SB);
         p.ws_bytes = decode_workspace_bytes(p.d, M, N, NT);
+        const int S = p.MB == 4 && decode_override().tn == 0 ? mid_m_prefill_split(p.d, K, NT, SB) : 0;
+        if (S > 0) {
+            p.kind = GemmPlan::kPrefill;
+            p.t = PrefillShape{1, 8, 4, 2, S};
+            p.ws_bytes = S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+        }
     } else {
         p.kind = GemmPlan::kPrefill;
         p.t = pick_prefill(fmt, M, N, NT, SB);

@@ -289,8 +289,8 @@ def test_workspace_size_is_a_split_k_partial_buffer():
         if b:
             S, rem = divmod(b, 4 * m * N)
             assert 2 <= S <= min(16, -(-K // 512)), (m, N, K, b)
-            if m > 64:
-                assert rem == 0, (m, N, K, b)
+            if m > 64 or rem == 0:  # prefill K split (also 33 <= m <= 64 on some narrower layers)
+                assert rem == 0 and m > 32, (m, N, K, b)
             else:
                 words = -(-N // 16)  # at most one group per 16-row n-tile
                 assert 8 <= rem <= 252 + 8 * words and (b - 8 * (rem // 8)) % 4 == 0, (m, N, K, b)
@@ -303,11 +303,21 @@ def test_workspace_size_is_a_split_k_partial_buffer():
     assert F.workspace_size(256, 57344, 8192, 0) == 0
     assert F.new_workspace(1000, 57344, 8192, 0) is None
     # 33 <= m <= 64 on a layer of >= 128 groups of 256 columns: whole-K prefill
-    # tiles, no workspace; the same m on a narrow layer keeps the decode kernel
+    # tiles, no workspace
     for m in (33, 48, 64):
         assert F.workspace_size(m, 57344, 8192, 0) == 0
         assert F.workspace_size(m, 32768, 544, 1) == 0
-    assert F.workspace_size(48, 8192, 8192, 0) > 0
+    # on narrower layers: the decode kernel while its grid fills the GPU and K
+    # is at most 16384 (O-shaped: decode planes plus arrival words), else 64-row
+    # prefill tiles split over the most workgroups one round holds (at most 8)
+    b = F.workspace_size(48, 8192, 8192, 0)
+    assert b > 0 and b % (4 * 48 * 8192) != 0
+    for (m, N, K), S in (((48, 10240, 8192), 6), ((33, 8200, 8192), 7), ((64, 8192, 28672), 8),
+                         ((40, 1000, 8192), 8)):
+        assert F.workspace_size(m, N, K, 0) == S * 4 * m * N, (m, N, K)
+    # m <= 32 keeps the decode kernel (no split, or planes plus arrival words)
+    b = F.workspace_size(24, 10240, 8192, 0)
+    assert b == 0 or b % (4 * 24 * 10240) != 0
 
 
 def test_gemm_rejects_small_or_misaligned_workspace_before_any_hip_call():

@@ -114,8 +114,10 @@ int fp4_unpack(const uint8_t* wq, const uint8_t* sq, int64_t N, int64_t K, int f
  * decode batch m = 16 has too few 16-row output tiles to give each of the
  * 256 compute units its own): each writes FP32
  * partial sums of its K range, which are added in a fixed order s = 0, 1, ...
- * For m <= 64 the last workgroup of each output group adds them (it finds out
- * through an 8-byte arrival word per group, after the partials); for m > 64 a
+ * With the decode kernels (m <= 64, except 33 <= m <= 64 on layers whose
+ * decode grid would fill the GPU poorly or whose K exceeds 16384) the last
+ * workgroup of each output group adds them (it finds out through an 8-byte
+ * arrival word per group, after the partials); with the prefill kernel a
  * second kernel does.  The size is about S * m * N * 4 bytes, or 0 when no
  * split is chosen.  The contents need no initialization (the arrival words
  * carry a tag unique to each launch, and the last workgroup of a group

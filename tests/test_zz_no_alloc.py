@@ -3,8 +3,8 @@ fp4_gemm, through the C ABI: the same kernels on the same inputs must give
 the same bits, and the oracle's tolerance, on two calls in a row whose second
 problem is smaller (the per-GPU scratch array keeps the first call's
 contents), for a decode K split (partials and arrival words in the scratch),
-a prefill K split (partials reduced by a second kernel) and a problem with no
-split."""
+a prefill K split (partials reduced by a second kernel; also the 64-row tiles
+33 <= m <= 64 takes on narrower layers) and a problem with no split."""
 
 import numpy as np
 import pytest
@@ -57,6 +57,7 @@ def _both(p):
     ((16, 10240, 8192, 0), (16, 1000, 8192, 0)),        # decode, K split finished in-kernel, then a smaller one
     ((256, 8192, 8192, 0), (100, 520, 2048, 1)),        # prefill K split (reduce kernel), then smaller
     ((16, 8192, 28672, 1), (7, 8200, 8192, 0)),         # down-shaped MXFP4 split, then a ragged NVFP4 one
+    ((48, 10240, 4096, 0), (40, 8200, 2048, 1)),        # 64-row prefill tiles with a K split (33 <= m <= 64)
 ])
 def test_noalloc_matches_gemm_on_two_calls(first, second):
     for i, (m, N, K, fmt) in enumerate((first, second)):

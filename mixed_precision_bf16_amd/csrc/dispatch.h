@@ -46,7 +46,7 @@ struct MoeArgs {
 // Compiled prefill shapes: X(WM, WN, MBW, TNW).
 #define FP4_PREFILL_SHAPES(X) \
     X(1, 4, 8, 2) X(1, 4, 8, 4) X(2, 2, 4, 4) X(2, 2, 4, 2) X(1, 4, 8, 1) X(2, 2, 4, 1) X(1, 4, 4, 4) \
-    X(1, 8, 8, 2) X(1, 8, 8, 1) X(1, 8, 4, 2)
+    X(1, 8, 8, 2) X(1, 8, 8, 1) X(1, 8, 4, 2) X(1, 8, 16, 2)
 
 // Launch one GEMM kernel on stream s (P: FP32 partials of a K split, else
 // null).  False when the shape is not compiled.  The decode kernel finishes

@@ -186,10 +186,20 @@ static bool prefill_compiled(const PrefillShape& t) {
 // n-tiles, so each dequantized fragment feeds 8 products and one wave's
 // vector work overlaps the other's matrix work (about 10 % faster than four
 // waves of four n-tiles); the K split S minimizes the rounds of workgroups
-// per unit of work (QKV 3, O and down 4, gate_up 1 at m = 256).  128 x 128
-// tiles with a smaller split measured faster on down on one box (121 against
-// 128 us) and slower on another (142 against 127 us), so they are not picked.
-// FP4GEMM_PREFILL="WM,WN,MBW,TNW,S" overrides it.
+// per unit of work (QKV 3, O and down 4 at m = 256).  Where m > 128 and the
+// 128-row tiles take more than one round without a split, 256-row tiles
+// (gemm_prefill_tall: eight waves of 16 m-blocks x 2 n-tiles, each weight
+// dequantized once per 256 rows) can cover the layer in fewer rounds: gate_up
+// 57344 x 8192 at m = 256 runs 224 tall workgroups in one round against 448
+// of 128 rows in two (MI355X, 60 launches back to back, the two plans
+// interleaved: 204.5 against 218.9 us; at m = 512 388.8 against 418.7 us;
+// same outputs bit for bit).  A tall round does the work of two 128-row
+// rounds in about 1.86 times the time; at m = 256 the split layers stay on
+// 128-row tiles (QKV 55.1 against 61.4 us for tall tiles with S = 6, O 46.2
+// against 57.7, down 111.8 against 116.3 with S = 8).  128 x 128 tiles with a smaller split measured faster on
+// down on one box (121 against 128 us) and slower on another (142 against
+// 127 us), so they are not picked.  FP4GEMM_PREFILL="WM,WN,MBW,TNW,S"
+// overrides the pick.
 static PrefillShape pick_prefill(int fmt, int64_t M, int64_t N, int NT, int SB) {
     (void)fmt;
     (void)N;
@@ -198,24 +208,34 @@ static PrefillShape pick_prefill(int fmt, int64_t M, int64_t N, int NT, int SB) 
         t.s = t.s < 1 ? 1 : (t.s > SB ? SB : t.s);
         return t;
     }
-    t = PrefillShape{1, 8, 8, 2, 1};
     // Time model fit to MI355X (m = 256): one workgroup per CU at a time
-    // (eight waves, 228 VGPRs); a round of workgroups over the whole K takes
-    // about 17 ns per K element, so a K split S runs ceil(blocks * S / 256)
-    // rounds of 1/S of that; a split also writes and reads S FP32 partials
-    // per output (about 5 TB/s) and pays the reduce launch (about 5 us).
-    const int64_t blocks = ((M + 127) / 128) * ((NT + 15) / 16);
+    // (eight waves); a round of 128 x 256 workgroups over the whole K takes
+    // about 17 ns per K element (a round of 256 x 256 ones 1.86 times that),
+    // so a K split S runs ceil(blocks * S / 256) rounds of 1/S of that; a
+    // split also writes and reads S FP32 partials per output (about 5 TB/s)
+    // and pays the reduce launch (about 5 us).
+    struct Cand {
+        PrefillShape shape;
+        int64_t blocks;
+        double t_round;
+    };
     const double t_round = 0.017e-6 * double(SB) * kScaleBlockK;
+    const int NG = (NT + 15) / 16;
+    const Cand cands[2] = {{PrefillShape{1, 8, 8, 2, 1}, ((M + 127) / 128) * NG, t_round},
+                           {PrefillShape{1, 8, 16, 2, 1}, ((M + 255) / 256) * NG, 1.86 * t_round}};
+    const int ncand = M > 128 ? 2 : 1;
     double best = 1e30;
-    for (int s = 1; s <= 8 && s <= SB; ++s) {
-        const double rounds = double((blocks * s + kCUs - 1) / kCUs);
-        const double split = s > 1 ? 5e-6 + double(s) * double(M) * double(N) * 8.0 / 5e12 : 0.0;
-        const double cost = rounds * t_round / s + split;
-        if (cost < best - 1e-9) {
-            best = cost;
-            t.s = s;
+    for (int c = 0; c < ncand; ++c)
+        for (int s = 1; s <= 8 && s <= SB; ++s) {
+            const double rounds = double((cands[c].blocks * s + kCUs - 1) / kCUs);
+            const double split = s > 1 ? 5e-6 + double(s) * double(M) * double(N) * 8.0 / 5e12 : 0.0;
+            const double cost = rounds * cands[c].t_round / s + split;
+            if (cost < best - 1e-9) {
+                best = cost;
+                t = cands[c].shape;
+                t.s = s;
+            }
         }
-    }
     return t;
 }
 

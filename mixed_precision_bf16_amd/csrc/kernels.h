@@ -980,6 +980,246 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_prefill(const uint16_t* __r
         }
 }
 
+// ------------------------------------------------------ tall prefill GEMM
+// 256-row tiles: a workgroup of NW waves computes a 256 (m) x 16 NW TNW (n)
+// tile, each wave over all 16 m-blocks and TNW n-tiles, so every weight is
+// dequantized once per 256 rows (half as often as with 128-row tiles) and
+// every dequantized fragment feeds 16 products.  Activations: two 64 KiB LDS
+// chunk buffers (256 rows x 128 K, XOR-swizzled by row as in gemm_prefill),
+// filled by DMA one chunk ahead; codes in a two-slot ring, issued with the
+// DMA.  An MFMA step (32 K) runs in 16 / FG groups of FG m-blocks whose
+// fragments are read one group ahead; the next step's weights are
+// dequantized during the current step.  Per 128-K chunk c (LDS buffer c % 2):
+//   steps 0..2 and step 3 up to its last group;
+//   wait for every load issued so far (the DMA and codes of chunk c+1, one
+//     chunk old), barrier: chunk c+1 is in LDS and every wave has read all
+//     of chunk c;
+//   DMA chunk c+2 into chunk c's buffer, codes of chunk c+2 into its slot;
+//   the last group of step 3, reading the first group of chunk c+1.
+template <int FMT, int ACT, int NW, int TNW, int FG, bool KTAIL>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_prefill_tall(
+    const uint16_t* __restrict__ A, const u32x4* __restrict__ wq, const uint8_t* __restrict__ sq,
+    uint16_t* __restrict__ C, float* __restrict__ P, int M, int N, int K, int KB, int SB, int NT, int S,
+    float alpha) {
+    typedef u32x4 SW;
+    constexpr int kThreads = 64 * NW, MBW = 16, BM = 256, BNT = NW * TNW;
+    constexpr int kGroups = MBW / FG;           // fragment groups per MFMA step
+    constexpr int kBuf = BM * 256;              // one LDS activation buffer (BM x 128 K x 2 B)
+    constexpr int kStage = BM * 16 / kThreads;  // 16-byte activation pieces per thread per chunk
+    constexpr int kScaleBlockBytes = scale_block_bytes<FMT>();
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
+    static_assert((kGroups == 2 || kGroups == 4) && kGroups % TNW == 0, "group / n-tile split");
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kBuf];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, j = lane >> 4;
+
+    // work item: K split ks (innermost), then an XCD-banded (m-tile, n-group) order
+    const int MT = (M + BM - 1) / BM, NG = (NT + BNT - 1) / BNT;
+    const int ks = blockIdx.x % S;
+    const int item = blockIdx.x / S;
+    const int total = MT * NG;
+    int L = item;
+    if (total % kXcdCount == 0 && S == 1)
+        L = (item % kXcdCount) * (total / kXcdCount) + item / kXcdCount;
+    const int mt = L % MT, ng = L / MT;
+    const int m0 = mt * BM;
+    const int tile0 = ng * BNT + wave * TNW;
+    const int sb0 = (ks * SB) / S, sb1 = ((ks + 1) * SB) / S;
+    const int c0 = 4 * sb0, clast = 4 * sb1 - 1;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(M * K * 2));
+    const int soff = scale_lane_offset<FMT>(r, j);
+    __amdgpu_buffer_rsrc_t rw[TNW], rs[TNW];
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt) {
+        const int t = min(tile0 + tt, NT - 1);
+        rw[tt] = make_rsrc(reinterpret_cast<const uint8_t*>(wq) + (size_t)t * KB * 1024, (uint32_t)KB * 1024u);
+        rs[tt] = make_rsrc(sq + (size_t)t * SB * kScaleBlockBytes, (uint32_t)(SB * kScaleBlockBytes));
+    }
+
+    // Activation DMA: piece q of the thread is LDS slot p = tid + kThreads q
+    // of the chunk buffer (row p / 16, physical column p % 16, logical column
+    // (p % 16) ^ (row % 16)); rows step by a multiple of 16 with q, so the
+    // logical column is the same for every piece of the thread.
+    const int arow = tid >> 4, acol = (tid & 15) ^ (arow & 15);
+    const uint32_t aoff = (uint32_t)((m0 + arow) * K + acol * 8) * 2u;
+    const uint32_t arow_step = (uint32_t)(kThreads / 16 * K) * 2u;
+    auto a_dma = [&](int chunk, int buf) {
+        chunk = min(chunk, clast);
+        const bool in_k = !KTAIL || chunk * kChunkK + acol * 8 < K;
+        const uint32_t off0 = aoff + (uint32_t)(chunk * kChunkK) * 2u;
+#pragma unroll
+        for (int q = 0; q < kStage; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void*)(lds_a + buf + (q * kThreads + 64 * wave) * 16), 16,
+                in_k ? off0 + q * arow_step : kOutOfRange, 0, 0, 0);
+    };
+    u32x4 wr[2][TNW];
+    auto w_issue = [&](auto slot_c, int chunk) {
+        constexpr int SL = decltype(slot_c)::value;
+        chunk = min(chunk, clast);
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt)
+            wr[SL][tt] = __builtin_amdgcn_raw_buffer_load_b128(rw[tt], lane * 16, chunk * 1024, kLoadStream);
+    };
+    auto lds_barrier = [] {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // fragments of group G (m-blocks FG G .. FG G + FG - 1) of step I of the
+    // chunk in the LDS buffer at byte offset buf
+    auto read_group = [&](auto i_c, auto g_c, int buf, u32x4 (&a)[FG]) {
+        constexpr int I = decltype(i_c)::value;
+        constexpr int G = decltype(g_c)::value;
+        const uint8_t* base = lds_a + buf + (G * FG * 16 + r) * 256 + (((4 * I + j) ^ r) << 4);
+#pragma unroll
+        for (int mb = 0; mb < FG; ++mb) a[mb] = *reinterpret_cast<const u32x4*>(base + mb * 16 * 256);
+    };
+
+    f32x4 acc[TNW][MBW];
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) acc[tt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 wcur[TNW], wnx[TNW];
+    // Products of group G with fragments a and wcur; n-tile G / (kGroups /
+    // TNW) of the next step (chunk position NTP, step NI, scales sn) is
+    // dequantized into wnx in the group that starts its share.
+    auto group = [&](auto t_c, auto i_c, auto g_c, const u32x4 (&a)[FG], const SW (&sn)[TNW]) {
+        constexpr int T = decltype(t_c)::value;
+        constexpr int I = decltype(i_c)::value;
+        constexpr int G = decltype(g_c)::value;
+        constexpr int NTP = I == 3 ? (T + 1) % 4 : T;
+        constexpr int NI = (I + 1) % 4;
+        if constexpr (G % (kGroups / TNW) == 0) {
+            constexpr int tt = G / (kGroups / TNW);
+            wnx[tt] = dequant_step<FMT, NTP, NI, ACT>(wr[NTP % 2][tt], sn[tt]);
+        }
+#pragma unroll
+        for (int mb = 0; mb < FG; ++mb)
+#pragma unroll
+            for (int tt = 0; tt < TNW; ++tt)
+                acc[tt][G * FG + mb] = mfma<ACT>(wcur[tt], a[mb], acc[tt][G * FG + mb]);
+    };
+    auto interleave = [] {
+        __builtin_amdgcn_sched_group_barrier(0x100, FG, 0);  // the next group's fragment reads first
+#pragma unroll
+        for (int q = 0; q < FG * TNW; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    u32x4 fa[FG], fb[FG];  // fragments of the even / odd groups
+    int b_cur = 0, b_nxt = kBuf;
+    // group G of MFMA step I of chunk position T (chunk base + T); on entry
+    // its fragments are in fa (G even) or fb (G odd)
+    auto one_group = [&](auto t_c, auto i_c, auto g_c, int base, const SW (&sn)[TNW]) {
+        constexpr int T = decltype(t_c)::value;
+        constexpr int I = decltype(i_c)::value;
+        constexpr int G = decltype(g_c)::value;
+        u32x4(&cur_f)[FG] = G % 2 == 0 ? fa : fb;
+        u32x4(&nxt_f)[FG] = G % 2 == 0 ? fb : fa;
+        if constexpr (G + 1 < kGroups) {
+            read_group(i_c, std::integral_constant<int, G + 1>{}, b_cur, nxt_f);
+        } else if constexpr (I < 3) {
+            read_group(std::integral_constant<int, I + 1>{}, I0{}, b_cur, nxt_f);
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            a_dma(base + T + 2, b_cur);
+            w_issue(std::integral_constant<int, T % 2>{}, base + T + 2);
+            const int b_free = b_cur;
+            b_cur = b_nxt;
+            b_nxt = b_free;
+            __builtin_amdgcn_sched_barrier(0);
+            read_group(I0{}, I0{}, b_cur, nxt_f);
+        }
+        group(t_c, i_c, g_c, cur_f, sn);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto step = [&](auto t_c, auto i_c, int base, const SW (&cur)[TNW], const SW (&nxt)[TNW]) {
+        constexpr int T = decltype(t_c)::value;
+        constexpr int I = decltype(i_c)::value;
+        const SW(&sn)[TNW] = T == 3 && I == 3 ? nxt : cur;
+        one_group(t_c, i_c, I0{}, base, sn);
+        one_group(t_c, i_c, I1{}, base, sn);
+        if constexpr (kGroups > 2) {
+            one_group(t_c, i_c, I2{}, base, sn);
+            one_group(t_c, i_c, I3{}, base, sn);
+        }
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt) wcur[tt] = wnx[tt];
+    };
+    auto chunk = [&](auto t_c, int base, const SW (&cur)[TNW], const SW (&nxt)[TNW]) {
+        step(t_c, I0{}, base, cur, nxt);
+        step(t_c, I1{}, base, cur, nxt);
+        step(t_c, I2{}, base, cur, nxt);
+        step(t_c, I3{}, base, cur, nxt);
+    };
+    SW sa[TNW], sbs[TNW];
+    auto block = [&](int sbx, const SW (&cur)[TNW], SW (&nxt)[TNW]) {
+        const int base = 4 * sbx;
+        const int nsb = min(sbx + 1, sb1 - 1);
+#pragma unroll
+        for (int tt = 0; tt < TNW; ++tt) nxt[tt] = load_scale_block<FMT>(rs[tt], soff, nsb);
+        chunk(I0{}, base, cur, nxt);
+        chunk(I1{}, base, cur, nxt);
+        chunk(I2{}, base, cur, nxt);
+        chunk(I3{}, base, cur, nxt);
+    };
+
+    // prologue: codes of chunks c0, c0+1 and the DMA of chunks c0, c0+1; the
+    // DMA of c0+1 is the youngest load, so everything older has landed
+    // after the wait
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt) sa[tt] = load_scale_block<FMT>(rs[tt], soff, sb0);
+    w_issue(I0{}, c0);
+    w_issue(I1{}, c0 + 1);
+    a_dma(c0, 0);
+    a_dma(c0 + 1, kBuf);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStage) : "memory");
+    lds_barrier();
+    read_group(I0{}, I0{}, b_cur, fa);
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt) wcur[tt] = dequant_step<FMT, 0, 0, ACT>(wr[0][tt], sa[tt]);
+    int sb = sb0;
+    for (; sb + 1 < sb1; sb += 2) {
+        block(sb, sa, sbs);
+        block(sb + 1, sbs, sa);
+    }
+    if (sb < sb1) block(sb, sa, sbs);
+    // no DMA may still write this workgroup's LDS after it exits
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+#pragma unroll
+    for (int tt = 0; tt < TNW; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+            const int m = m0 + mb * 16 + r, n0 = (tile0 + tt) * kTileN + 4 * j;
+            if (P == nullptr) {
+                store_frag<ACT>(C, acc[tt][mb] * alpha, m, n0, M, N);
+            } else if (m < M) {  // FP32 partials for the reduce kernel
+                float* dst = P + ((size_t)ks * M + m) * N + n0;
+                if ((N & 3) == 0 && n0 + 3 < N) {
+                    *reinterpret_cast<f32x4*>(dst) = acc[tt][mb];
+                } else {
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + e < N) dst[e] = acc[tt][mb][e];
+                }
+            }
+        }
+}
+
 // ------------------------------------------------------------ quantizer
 // Offline quantizer: BF16 weights -> E2M1 codes (two per byte, element 2j in
 // the low nibble) and one scale byte per G-element block, in the source

@@ -4,12 +4,14 @@ the full CPU oracle.
 The shapes are drawn (one fixed seed) across every regime the dispatch
 distinguishes: the decode kernel with 16-, 32- and 64-row activation blocks
 (with and without a K split), the 64-row prefill tiles of wide layers at
-33 <= m <= 64, and the prefill kernel with and without a K split; ragged m, N
+33 <= m <= 64, the prefill kernel with and without a K split, and its
+256-row tiles on wide layers at m > 128; ragged m, N
 and K (K any multiple of the group size, so K tails inside a 512-K scale
 block), both weight formats, both activation types and, for some cases, a
 per-tensor alpha.  Every output is compared with oracle.gemm_reference (scaled
 by alpha where given) under the GEMM tolerance.  Sizes are bounded so that
-the float64 oracle finishes each case in well under a second.
+the float64 oracle finishes each random case in well under a second and each
+256-row tile case in a few seconds.
 """
 
 import numpy as np
@@ -68,10 +70,33 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+# 256-row prefill tiles (gemm_prefill_tall): m > 128 on layers wide enough
+# that 128-row tiles take a second round of workgroups; ragged m inside one
+# and two 256-row tiles, a partial last group of n-tiles, K tails inside a
+# 512-K scale block, and a K split (long K at m = 129).
+TALL_CASES = [
+    (256, 32768 + 16, 512, 0, "bf16", 1.0),
+    (129, 40000, 1088, 1, "f16", 1.0),
+    (255, 57344, 512, 0, "bf16", 2.5),
+    (500, 30000, 528, 0, "bf16", 1.0),
+    (200, 36000, 1024 + 32, 1, "bf16", 0.75),
+    (129, 8192, 28672, 0, "bf16", 1.0),
+]
+
+
 @pytest.mark.parametrize("m,N,K,fmt,act,alpha", CASES)
 def test_random_shape_full_oracle(m, N, K, fmt, act, alpha):
+    _check("random", m, N, K, fmt, act, alpha)
+
+
+@pytest.mark.parametrize("m,N,K,fmt,act,alpha", TALL_CASES)
+def test_tall_prefill_full_oracle(m, N, K, fmt, act, alpha):
+    _check("tall", m, N, K, fmt, act, alpha)
+
+
+def _check(tag, m, N, K, fmt, act, alpha):
     seed = (m * 1000003 + N * 7919 + K * 31 + fmt) % (1 << 31)
-    print("[case] random", m, N, K, fmt, act, alpha, flush=True)
+    print("[case]", tag, m, N, K, fmt, act, alpha, flush=True)
     p = synth.make_random(m, N, K, fmt, seed=seed, act=act)
     wq, sq = F.upload(*F.repack(p.codes, p.scales, N, K, fmt))
     tdt = torch.bfloat16 if act == "bf16" else torch.float16

@@ -1043,9 +1043,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // Activation DMA: piece q of the thread is LDS slot p = tid + kThreads q
     // of the chunk buffer (row p / 16, physical column p % 16, logical column
     // (p % 16) ^ (row % 16)); rows step by a multiple of 16 with q, so the
-    // logical column is the same for every piece of the thread.
+    // logical column is the same for every piece of the thread.  Offsets are
+    // 32-bit unsigned: the host bounds round_up(M, 128) * K * 2 below 2^31,
+    // so rows below M are exact; a padding row of the last 256-row tile may
+    // wrap, and its load then reads zeros or another row's values that only
+    // feed outputs at rows >= M, which are never stored.
     const int arow = tid >> 4, acol = (tid & 15) ^ (arow & 15);
-    const uint32_t aoff = (uint32_t)((m0 + arow) * K + acol * 8) * 2u;
+    const uint32_t aoff = ((uint32_t)(m0 + arow) * (uint32_t)K + (uint32_t)(acol * 8)) * 2u;
     const uint32_t arow_step = (uint32_t)(kThreads / 16 * K) * 2u;
     auto a_dma = [&](int chunk, int buf) {
         chunk = min(chunk, clast);

@@ -474,12 +474,14 @@ def test_split_k_decode_captured_in_a_graph_replays(m, N, K, fmt):
 
 
 @pytest.mark.parametrize("m,N,K,fmt,act", [(256, 8192, 2048, 0, "bf16"), (200, 520, 2560, 1, "f16"),
-                                           (48, 10240, 4096, 0, "bf16"), (40, 8200, 2048, 1, "f16")])
+                                           (48, 10240, 4096, 0, "bf16"), (40, 8200, 2048, 1, "f16"),
+                                           (129, 8192, 28672, 0, "bf16")])
 def test_prefill_split_captured_in_a_graph_replays(m, N, K, fmt, act):
     # a prefill GEMM with a K split (FP32 partials in the workspace, then the
     # reduce kernel; also the 64-row tiles 33 <= m <= 64 takes on narrower
-    # layers), captured once and replayed with new activations and eager work
-    # in between: every replay equals an eager call
+    # layers and the 256-row tiles of a long-K layer at m = 129), captured
+    # once and replayed with new activations and eager work in between: every
+    # replay equals an eager call
     need = F.workspace_size(m, N, K, fmt)
     assert need > 0, "expected a K split"
     _say("prefill graph replay", m, N, K, fmt, act)

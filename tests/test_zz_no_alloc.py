@@ -4,7 +4,8 @@ the same bits, and the oracle's tolerance, on two calls in a row whose second
 problem is smaller (the per-GPU scratch array keeps the first call's
 contents), for a decode K split (partials and arrival words in the scratch),
 a prefill K split (partials reduced by a second kernel; also the 64-row tiles
-33 <= m <= 64 takes on narrower layers) and a problem with no split."""
+33 <= m <= 64 takes on narrower layers and the 256-row tiles of a long-K layer
+at m = 129) and a problem with no split."""
 
 import numpy as np
 import pytest
@@ -58,6 +59,7 @@ def _both(p):
     ((256, 8192, 8192, 0), (100, 520, 2048, 1)),        # prefill K split (reduce kernel), then smaller
     ((16, 8192, 28672, 1), (7, 8200, 8192, 0)),         # down-shaped MXFP4 split, then a ragged NVFP4 one
     ((48, 10240, 4096, 0), (40, 8200, 2048, 1)),        # 64-row prefill tiles with a K split (33 <= m <= 64)
+    ((129, 8192, 28672, 0), (256, 32784, 512, 1)),      # 256-row prefill tiles with a K split, then without
 ])
 def test_noalloc_matches_gemm_on_two_calls(first, second):
     for i, (m, N, K, fmt) in enumerate((first, second)):

@@ -1312,6 +1312,45 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     uint32_t out[G / 8];
 #pragma unroll
     for (int w = 0; w < G / 8; ++w) out[w] = 0;
+    if constexpr (FMT == 1) {
+        // alpha a power of two: S = 2^es is one too, so q = |x| / S is exact
+        // and the gfx950 FP32 -> FP4 convert with S as its (E8M0) scale gives
+        // the nearest E2M1 code with ties to the even mantissa, saturating at
+        // 6 (checked on the device against this rule for every BF16 value and
+        // scale bytes 0 .. 254); it differs only in writing the sign bit on
+        // codes of magnitude 0 and in converting NaN to code 7, both undone.
+        const uint32_t ab = __float_as_uint(alpha);
+        const int es = int((ab >> 23) & 0xFF) - 127 + int(sb) - 127;  // log2 S when alpha = 2^(exp)
+        if ((ab & 0x007FFFFFu) == 0u && ((ab >> 23) & 0xFF) != 0u && es >= -127 && es <= 127) {
+            const float sc = __uint_as_float((uint32_t)(es + 127) << 23);
+            bool nan_any = false;
+#pragma unroll
+            for (int i = 0; i < G / 2; ++i) nan_any |= __builtin_isunordered(x[2 * i], x[2 * i + 1]);
+#pragma unroll
+            for (int w = 0; w < G / 8; ++w) {
+                // FP32 operands (the BF16 values, exact): a bit cast of single
+                // elements of the loaded vectors into the BF16 form was
+                // mis-folded by clang into one element for all four converts
+                uint32_t o = 0;
+                o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, x[8 * w + 0], x[8 * w + 1], sc, 0);
+                o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, x[8 * w + 2], x[8 * w + 3], sc, 1);
+                o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, x[8 * w + 4], x[8 * w + 5], sc, 2);
+                o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, x[8 * w + 6], x[8 * w + 7], sc, 3);
+                // keep a nibble's sign bit only where its magnitude is non-zero
+                // (magnitude + 7 carries into bit 3 exactly when it is >= 1)
+                const uint32_t mag = o & 0x77777777u;
+                out[w] = mag | (o & ((mag + 0x77777777u) & 0x88888888u));
+            }
+            if (nan_any) {
+#pragma unroll
+                for (int i = 0; i < G; ++i)
+                    if (__builtin_isnan(x[i])) out[i / 8] &= ~(0xFu << (4 * (i % 8)));
+            }
+            *reinterpret_cast<u32x4*>(codes + g * (G / 2)) = u32x4{out[0], out[1], out[2], out[3]};
+            scales[g] = (uint8_t)sb;
+            return;
+        }
+    }
     // With alpha a power of two, S has at most 4 significant bits and x at
     // most 8, so q = fl(|x| / S) lies on the same side of every midpoint c
     // (at most 3 significant bits) as |x| does of c x S, which is exact in

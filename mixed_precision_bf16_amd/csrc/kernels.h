@@ -1312,6 +1312,50 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     uint32_t out[G / 8];
 #pragma unroll
     for (int w = 0; w < G / 8; ++w) out[w] = 0;
+    if constexpr (FMT == 0) {
+        // alpha a power of two: S = 2^es x M with M in [1, 2) of at most 4
+        // significant bits (the E4M3 mantissa).  y = x x rcp(M) is within 4
+        // ulps of x / M; a quotient that is not a midpoint (at most 3
+        // significant bits) lies at least 2^-8 / 300 relative, over 100 ulps,
+        // from every midpoint (as for the thresholds below), so y decides like
+        // x / M once values within 4 ulps of a 3-significant-bit number are
+        // snapped to it (that restores an exact midpoint and moves no other
+        // quotient across one).  Then the FP32 -> FP4 convert with scale 2^es
+        // rounds y / 2^es as the rule does (see the MXFP4 branch).
+        const uint32_t ab = __float_as_uint(alpha), Sb = __float_as_uint(S);
+        if ((ab & 0x007FFFFFu) == 0u && ((ab >> 23) & 0xFF) != 0u && ((Sb >> 23) & 0xFF) != 0u) {
+            const float sc = __uint_as_float(Sb & 0x7F800000u);  // 2^es (S is normal: >= 2^-109)
+            const float r = __builtin_amdgcn_rcpf(__uint_as_float((Sb & 0x007FFFFFu) | 0x3F800000u));
+            bool nan_any = false;
+#pragma unroll
+            for (int i = 0; i < G / 2; ++i) nan_any |= __builtin_isunordered(x[2 * i], x[2 * i + 1]);
+            float y[G];
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const uint32_t yb = __float_as_uint(x[i] * r);
+                const uint32_t y3 = (yb + 0x00100000u) & 0xFFE00000u;  // nearest with 3 significant bits
+                y[i] = __uint_as_float(yb - y3 + 4u <= 8u ? y3 : yb);  // |yb - y3| <= 4
+            }
+#pragma unroll
+            for (int w = 0; w < G / 8; ++w) {
+                uint32_t o = 0;
+                o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[8 * w + 0], y[8 * w + 1], sc, 0);
+                o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[8 * w + 2], y[8 * w + 3], sc, 1);
+                o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[8 * w + 4], y[8 * w + 5], sc, 2);
+                o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[8 * w + 6], y[8 * w + 7], sc, 3);
+                const uint32_t mag = o & 0x77777777u;
+                out[w] = mag | (o & ((mag + 0x77777777u) & 0x88888888u));
+            }
+            if (nan_any) {
+#pragma unroll
+                for (int i = 0; i < G; ++i)
+                    if (__builtin_isnan(x[i])) out[i / 8] &= ~(0xFu << (4 * (i % 8)));
+            }
+            *reinterpret_cast<u32x2*>(codes + g * (G / 2)) = u32x2{out[0], out[1]};
+            scales[g] = (uint8_t)sb;
+            return;
+        }
+    }
     if constexpr (FMT == 1) {
         // alpha a power of two: S = 2^es is one too, so q = |x| / S is exact
         // and the gfx950 FP32 -> FP4 convert with S as its (E8M0) scale gives

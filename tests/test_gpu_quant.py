@@ -75,6 +75,49 @@ def test_quantize_bit_exact(fmt, N, K, alpha):
     assert np.array_equal(c, want_c), np.argwhere(c != want_c)[:5]
 
 
+def _midpoint_weights(N, K, fmt, alpha, seed):
+    """BF16 weight bits whose every block has a chosen scale (an E4M3 value,
+    or a power of two for MXFP4: the block maximum is 6 x scale x alpha) and
+    whose other elements are E2M1 values and exact midpoints between them
+    times that scale, a quarter of them moved to a BF16 neighbour: the cases
+    where a decision by a rounded quotient would go wrong."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    G = 16 if fmt == 0 else 32
+    nb = K // G
+    vals = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    if fmt == 0:
+        e4 = oracle.e4m3_value(np.arange(1, 0x7F))
+        s = e4[rng.integers(0, len(e4), size=(N, nb))]
+    else:
+        s = np.exp2(rng.integers(-20, 20, size=(N, nb)).astype(np.float64))
+    w = vals[rng.integers(0, len(vals), size=(N, nb, G))] * (s * alpha)[..., None]
+    w[..., 0] = 6.0 * s * alpha
+    w *= np.where(rng.random((N, nb, G)) < 0.5, -1.0, 1.0)
+    bits = torch.from_numpy(w.astype(np.float32).reshape(N, K)).to(torch.bfloat16).view(torch.int16).numpy()
+    bits = bits.view(np.uint16).copy()
+    step = np.where(rng.random(bits.shape) < 0.5, 1, -1)
+    nudge = rng.random(bits.shape) < 0.25
+    return np.where(nudge, bits.astype(np.int64) + step, bits).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("alpha", [1.0, 2.0 ** -7, 2.0 ** 20])
+def test_quantize_midpoint_blocks_bit_exact(fmt, alpha):
+    """With alpha a power of two the quantizer decides by the hardware FP32 ->
+    FP4 convert (NVFP4: on x / M snapped to 3 significant bits near a
+    midpoint); blocks made of exact midpoints and their neighbours under
+    every scale meet the oracle's nearest-even rule bit for bit."""
+    bits = _midpoint_weights(128, 1024, fmt, alpha, seed=31 + fmt)
+    _say("quantize midpoints", fmt, alpha)
+    want_c, want_s = oracle.quantize_reference(bits, fmt, alpha)
+    W = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    c, s = F.quantize(W, fmt, alpha)
+    torch.cuda.synchronize()
+    c, s = c.cpu().numpy(), s.cpu().numpy()
+    assert np.array_equal(s, want_s), np.argwhere(s != want_s)[:5]
+    assert np.array_equal(c, want_c), np.argwhere(c != want_c)[:5]
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_quantize_then_gemm_parity(fmt):
     """Device-quantized weights through repack and the GEMM: within the

@@ -511,6 +511,10 @@ static int moe_impl(const void* A, const void* wq, const void* sq, const int32_t
     return launch_status();
 }
 
+// Largest number of G-element blocks one quantizer launch covers (one thread
+// each, so far below the 2^32 work-items a dispatch can count).
+constexpr int64_t kQuantSliceGroups = int64_t(1) << 26;
+
 static int quantize_impl(const void* W, void* codes, void* scales, int64_t N, int64_t K, int format, float alpha,
                          void* stream) {
     if (format != FP4_NVFP4 && format != FP4_MXFP4) return FP4_ERR_FORMAT;
@@ -522,17 +526,27 @@ static int quantize_impl(const void* W, void* codes, void* scales, int64_t N, in
     if (!(alpha > 0.0f) || !alpha_ok(alpha)) return FP4_ERR_VALUE;
     int st = check_device();
     if (st != FP4_OK) return st;
-    const int64_t groups = N * (K / G);
+    // One thread per G-element block.  A dispatch counts its work-items in 32
+    // bits, so the rows go out in slices of at most kQuantSliceGroups blocks
+    // (whole rows; a row has at most 2^20 blocks).
+    const int64_t gpr = K / G;
+    const int64_t rows_per = std::max<int64_t>(1, kQuantSliceGroups / gpr);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const dim3 grid((unsigned)((groups + 255) / 256)), block(256);
-    if (format == FP4_NVFP4)
-        quantize_kernel<0><<<grid, block, 0, s>>>((const uint16_t*)W, (uint8_t*)codes, (uint8_t*)scales, groups,
-                                                  alpha, K / G, K / G);
-    else
-        quantize_kernel<1><<<grid, block, 0, s>>>((const uint16_t*)W, (uint8_t*)codes, (uint8_t*)scales, groups,
-                                                  alpha, K / G, K / G);
-    return launch_status();
+    for (int64_t r0 = 0; r0 < N; r0 += rows_per) {
+        const int64_t groups = std::min(rows_per, N - r0) * gpr;
+        const uint16_t* w = static_cast<const uint16_t*>(W) + r0 * K;
+        uint8_t* c = static_cast<uint8_t*>(codes) + r0 * (K / 2);
+        uint8_t* sc = static_cast<uint8_t*>(scales) + r0 * gpr;
+        const dim3 grid((unsigned)((groups + 255) / 256)), block(256);
+        if (format == FP4_NVFP4)
+            quantize_kernel<0><<<grid, block, 0, s>>>(w, c, sc, groups, alpha, gpr, gpr);
+        else
+            quantize_kernel<1><<<grid, block, 0, s>>>(w, c, sc, groups, alpha, gpr, gpr);
+        st = launch_status();
+        if (st != FP4_OK) return st;
+    }
+    return FP4_OK;
 }
 
 // Native FP4 path: workspace = quantized activations (m rows of Kp / 2 code

@@ -75,6 +75,45 @@ def test_quantize_bit_exact(fmt, N, K, alpha):
     assert np.array_equal(c, want_c), np.argwhere(c != want_c)[:5]
 
 
+@pytest.mark.parametrize("fmt,N,K", [(0, 163877, 16384), (1, 260, 1 << 24)])
+def test_quantize_many_launches_bit_exact(fmt, N, K):
+    """More G-element blocks than one quantizer launch covers (the library
+    launches at most 2^26 blocks, whole rows, at a time; here 2.5 and 2 such
+    slices plus a ragged one, the second at the largest K).  The weights are
+    seeded random BF16 made on the device; at the first and last row, at
+    random rows and at the rows on both sides of each slice boundary, the
+    first and last 4096 elements are replaced by host-drawn blocks (with the
+    special values of _weights), whose codes and scales must match the oracle
+    bit for bit."""
+    G = 16 if fmt == 0 else 32
+    SEG = 4096
+    rows_per = (1 << 26) // (K // G)
+    rows = {0, N - 1}
+    for b in range(rows_per, N, rows_per):
+        rows.update((b - 1, b))
+    rows.update(int(x) for x in np.random.Generator(np.random.PCG64(N)).choice(N, 6, replace=False))
+    rows = sorted(rows)
+    _say("quantize, several launches", fmt, N, K, rows)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(N + fmt)
+    W = torch.randn((N, K), dtype=torch.bfloat16, device="cuda", generator=gen)
+    seg = _weights(2 * len(rows), SEG, fmt, seed=3 * N + fmt)
+    for i, r in enumerate(rows):
+        W[r, :SEG].copy_(torch.from_numpy(seg[2 * i].view(np.int16)).view(torch.bfloat16))
+        W[r, K - SEG:].copy_(torch.from_numpy(seg[2 * i + 1].view(np.int16)).view(torch.bfloat16))
+    c, s = F.quantize(W, fmt)
+    torch.cuda.synchronize()
+    del W
+    idx = torch.tensor(rows, device="cuda")
+    c, s = c.index_select(0, idx).cpu().numpy(), s.index_select(0, idx).cpu().numpy()
+    torch.cuda.empty_cache()
+    got_c = np.stack([c[:, :SEG // 2], c[:, K // 2 - SEG // 2:]], axis=1).reshape(2 * len(rows), SEG // 2)
+    got_s = np.stack([s[:, :SEG // G], s[:, K // G - SEG // G:]], axis=1).reshape(2 * len(rows), SEG // G)
+    want_c, want_s = oracle.quantize_reference(seg, fmt, 1.0)
+    assert np.array_equal(got_s, want_s), np.argwhere(got_s != want_s)[:5]
+    assert np.array_equal(got_c, want_c), np.argwhere(got_c != want_c)[:5]
+
+
 def _midpoint_weights(N, K, fmt, alpha, seed):
     """BF16 weight bits whose every block has a chosen scale (an E4M3 value,
     or a power of two for MXFP4: the block maximum is 6 x scale x alpha) and

@@ -149,3 +149,62 @@ def test_moe_ids_out_of_range_are_skipped():
     assert set(np.flatnonzero(written)) == set(keep.tolist()) and ref_ids is not None
     assert np.isnan(y[~written]).all()
     assert oracle.check_tolerance(_bits(out)[written], y_ref[written], bound[written]).all()
+
+
+def test_moe_grid_near_its_limit_full_oracle():
+    """4096 experts (the largest E) and 960000 assignments with one activation
+    row each: 960000 / 16 + 4096 = 64096 row blocks of the 65535 a launch may
+    have; every listed row against the full MoE oracle."""
+    p = synth.make_moe(240000, 4, 4096, 64, 256, 1, seed=4096, per_assignment_a=True)
+    assert p.sorted_ids.size // 16 + p.E <= 65535
+    _say("moe grid near its limit", p.name)
+    check(p, run_moe(p))
+
+
+def test_moe_experts_past_4_gib_sampled():
+    """4096 NVFP4 experts of 2048 x 2048: 8 GiB of packed codes, so expert
+    offsets pass 2^31 and 2^32 bytes.  The packed experts are seeded random
+    bytes made on the device (valid scale bytes only); a sample of experts
+    (the first, the last, those around the 2^31- and 2^32-byte offsets and
+    random ones, each with at least one assignment) get host-drawn weights,
+    and their rows are checked against the MoE oracle on those experts."""
+    T, topk, E, N, K, fmt = 8192, 4, 4096, 2048, 2048, 0
+    sorted_ids, offsets, topw = synth.moe_routing(T, topk, E, seed=44)
+    counts = np.diff(offsets)
+    nw, ns = F.repack_size(N, K, fmt)
+    edges = [x for b in (1 << 31, 1 << 32) for x in (b // nw - 1, b // nw)]
+    rng = np.random.Generator(np.random.PCG64(45))
+    want = sorted({0, 1, E - 2, E - 1, *edges, *(int(x) for x in rng.choice(E, 20, replace=False))})
+    sample = [e for e in want if counts[e] > 0]
+    assert any(e * nw >= (1 << 32) for e in sample) and any((1 << 31) <= e * nw < (1 << 32) for e in sample)
+    _say("moe experts past 4 GiB", T, topk, E, N, K, sample)
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(46)
+    wq = torch.randint(0, 256, (E * nw,), dtype=torch.uint8, device="cuda", generator=gen)
+    sq = torch.randint(0x18, 0x49, (E * ns,), dtype=torch.uint8, device="cuda", generator=gen)
+    codes, scales = [], []
+    for i, e in enumerate(sample):
+        w = synth.make_random(1, N, K, fmt, seed=500 + i)
+        twq, tsq = F.repack(w.codes, w.scales, N, K, fmt)
+        wq[e * nw:(e + 1) * nw].copy_(torch.from_numpy(twq))
+        sq[e * ns:(e + 1) * ns].copy_(torch.from_numpy(tsq))
+        codes.append(w.codes)
+        scales.append(w.scales)
+    a_bits = synth.make_random(T, 1, K, fmt, seed=47).a_bits
+    A = torch.from_numpy(np.ascontiguousarray(a_bits).view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.full((T * topk, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    F.moe_gemm(A, wq, sq, torch.from_numpy(sorted_ids).cuda(), torch.from_numpy(offsets).cuda(), N, K, fmt, E,
+               topk, T * topk, topk_weights=torch.from_numpy(topw).cuda(), out=out)
+    torch.cuda.synchronize()
+    del wq, sq
+    y_bits = _bits(out)
+    del out
+    torch.cuda.empty_cache()
+    assert np.isfinite(oracle.bf16_bits_to_f64(y_bits)).all(), "every assignment row is written and finite"
+    sub_ids = np.concatenate([sorted_ids[offsets[e]:offsets[e + 1]] for e in sample])
+    sub_off = np.concatenate([[0], np.cumsum([counts[e] for e in sample])]).astype(np.int32)
+    y_ref, bound, written = oracle.moe_reference(a_bits, np.stack(codes), np.stack(scales), sub_ids, sub_off, topw,
+                                                 topk, T * topk, K, fmt)
+    ok = oracle.check_tolerance(y_bits[written], y_ref[written], bound[written])
+    assert ok.all(), f"{int((~ok).sum())} of {ok.size} outputs of the sampled experts out of tolerance"

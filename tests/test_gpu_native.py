@@ -175,3 +175,28 @@ def test_native_split_captured_in_a_graph_replays():
         assert np.array_equal(got, want), f"replay {rep} differs from the eager call"
     a_bits = A.view(torch.int16).cpu().numpy().view(np.uint16)
     check(synth.Problem("native_graph", m, N, K, 1, a_bits, p.codes, p.scales, 31), got)
+
+
+def test_native_at_its_activation_limit():
+    """m = 4095 rows of K = 2^20 - 512: the quantized activations (m rounded
+    to 128, Kp / 2 bytes per row) are 1 MiB short of 2^31 bytes and A is
+    8.6 GB.  A's rows are drawn from 32 distinct seeded rows (the activation
+    quantizer works per row), so the oracle computes 32 rows and every output
+    row is held to its source row's tolerance."""
+    m, N, K = 4095, 24, (1 << 20) - 512
+    assert -(-m // 128) * 128 * K // 2 < (1 << 31) <= -(-m // 128) * 128 * (K + 512) // 2
+    pool = synth.make_random(32, N, K, 1, seed=4095)
+    src = np.random.Generator(np.random.PCG64(m)).integers(0, 32, size=m)
+    _say("native at its activation limit", m, N, K)
+    wq, sq = F.native_repack(pool.codes, pool.scales, N, K)
+    rows = torch.from_numpy(np.ascontiguousarray(pool.a_bits).view(np.int16)).cuda().view(torch.bfloat16)
+    A = rows.index_select(0, torch.from_numpy(src).cuda()).contiguous()
+    y = F.gemm_native(A, wq.cuda(), sq.cuda(), N, K)
+    torch.cuda.synchronize()
+    del A
+    y_bits = _bits(y)
+    del y
+    torch.cuda.empty_cache()
+    y_ref, bound = oracle.native_reference(pool.a_bits, pool.codes, pool.scales, K)
+    ok = oracle.check_tolerance(y_bits, y_ref[src], bound[src])
+    assert ok.all(), f"{int((~ok).sum())} of {ok.size} outputs out of tolerance"

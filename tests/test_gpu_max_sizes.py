@@ -1,4 +1,4 @@
-"""fp4_gemm at the size limits the boundary accepts (include/fp4gemm.h: K <= 2^20,
+"""fp4_gemm and fp4_dequant at the size limits the boundary accepts (include/fp4gemm.h: K <= 2^20,
 N <= 2^24, and the bytes of A and Y, m rounded up to the kernel's row block,
 below 2^31), against the CPU oracle.
 
@@ -102,7 +102,41 @@ def _sample_tiles(NT, tile_bytes, rng, extra=24):
         t = edge // tile_bytes
         tiles.update(x for x in (t - 1, t, t + 1) if 0 <= x < NT)
     tiles.update(int(x) for x in rng.choice(NT, size=min(extra, NT), replace=False))
-    return sorted(tiles)
+    return sorted(t for t in tiles if 0 <= t < NT)
+
+
+def _weights_with_sampled_tiles(N, K, fmt, seed):
+    """Packed weights on the device: seeded random bytes (valid scale bytes
+    only) with host-drawn 16-row tiles repacked into the sampled slots.
+    Returns (wq, sq, codes, scales, cols): the host codes and scales of the
+    sampled rows and their column (row of W) indices."""
+    G = 16 if fmt == 0 else 32
+    Kp = -(-K // 512) * 512
+    NT = -(-N // 16)
+    tile_codes, tile_scales = Kp * 8, (Kp // 512) * (512 if fmt == 0 else 256)
+    wq_bytes, sq_bytes = F.repack_size(N, K, fmt)
+    assert (wq_bytes, sq_bytes) == (NT * tile_codes, NT * tile_scales)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    wq = torch.randint(0, 256, (wq_bytes,), dtype=torch.uint8, device="cuda", generator=gen)
+    lo, hi = (0x18, 0x48) if fmt == 0 else (127 - 6, 127 + 2)
+    sq = torch.randint(lo, hi + 1, (sq_bytes,), dtype=torch.uint8, device="cuda", generator=gen)
+    tiles = _sample_tiles(NT, tile_codes, np.random.Generator(np.random.PCG64(seed + N)))
+    codes, scales, cols = [], [], []
+    for i, t in enumerate(tiles):
+        rows = min(16, N - 16 * t)
+        tp = synth.make_random(1, rows, K, fmt, seed=5000 + 31 * i + seed)
+        twq, tsq = F.repack(tp.codes, tp.scales, rows, K, fmt)
+        assert twq.size == tile_codes and tsq.size == tile_scales
+        wq[t * tile_codes:(t + 1) * tile_codes].copy_(torch.from_numpy(twq))
+        sq[t * tile_scales:(t + 1) * tile_scales].copy_(torch.from_numpy(tsq))
+        codes.append(tp.codes)
+        scales.append(tp.scales)
+        cols.append(16 * t + np.arange(rows))
+    codes, scales, cols = np.concatenate(codes), np.concatenate(scales), np.concatenate(cols)
+    assert scales.shape[1] == K // G
+    print("[tiles]", tiles[:4], "..", tiles[-3:], flush=True)
+    return wq, sq, codes, scales, cols
 
 
 @pytest.mark.parametrize("m,N,K,fmt", [
@@ -114,35 +148,7 @@ def _sample_tiles(NT, tile_bytes, rng, extra=24):
 def test_largest_n_sampled_tiles(m, N, K, fmt):
     assert N <= NMAX and m * N * 2 < (1 << 31)
     print("[case] largest N", m, N, K, fmt, flush=True)
-    G = 16 if fmt == 0 else 32
-    Kp = -(-K // 512) * 512
-    NT = -(-N // 16)
-    tile_codes, tile_scales = Kp * 8, (Kp // 512) * (512 if fmt == 0 else 256)
-    wq_bytes, sq_bytes = F.repack_size(N, K, fmt)
-    assert (wq_bytes, sq_bytes) == (NT * tile_codes, NT * tile_scales)
-
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(1000 + m)
-    wq = torch.randint(0, 256, (wq_bytes,), dtype=torch.uint8, device="cuda", generator=gen)
-    lo, hi = (0x18, 0x48) if fmt == 0 else (127 - 6, 127 + 2)
-    sq = torch.randint(lo, hi + 1, (sq_bytes,), dtype=torch.uint8, device="cuda", generator=gen)
-
-    rng = np.random.Generator(np.random.PCG64(m + N))
-    tiles = _sample_tiles(NT, tile_codes, rng)
-    codes, scales, cols = [], [], []
-    for i, t in enumerate(tiles):
-        rows = min(16, N - 16 * t)
-        tp = synth.make_random(1, rows, K, fmt, seed=5000 + 31 * i + m)
-        twq, tsq = F.repack(tp.codes, tp.scales, rows, K, fmt)
-        assert twq.size == tile_codes and tsq.size == tile_scales
-        wq[t * tile_codes:(t + 1) * tile_codes].copy_(torch.from_numpy(twq))
-        sq[t * tile_scales:(t + 1) * tile_scales].copy_(torch.from_numpy(tsq))
-        codes.append(tp.codes)
-        scales.append(tp.scales)
-        cols.append(16 * t + np.arange(rows))
-    codes, scales, cols = np.concatenate(codes), np.concatenate(scales), np.concatenate(cols)
-    assert scales.shape[1] == K // G
-
+    wq, sq, codes, scales, cols = _weights_with_sampled_tiles(N, K, fmt, 1000 + m)
     a_bits = synth.make_random(m, 1, K, fmt, seed=77 + m).a_bits
     C = F.gemm(_a_dev(a_bits, "bf16"), wq, sq, N, K, fmt)
     torch.cuda.synchronize()
@@ -151,4 +157,25 @@ def test_largest_n_sampled_tiles(m, N, K, fmt):
     del C, wq, sq
     torch.cuda.empty_cache()
     y_ref, bound = oracle.gemm_reference(a_bits, codes, scales, K, fmt)
-    _assert_close(got, y_ref, bound, "bf16", f"largest N, tiles {tiles[:4]}..{tiles[-2:]}")
+    _assert_close(got, y_ref, bound, "bf16", "largest N")
+
+
+@pytest.mark.parametrize("N,K,fmt", [(NMAX, 512, 0), (16, KMAX, 1), (40, KMAX - 16, 0)])
+def test_dequant_at_the_limits_bit_exact(N, K, fmt):
+    """fp4_dequant (the weights exactly as the GEMM feeds them to the matrix
+    core) at the largest N (a 16 GiB output) and the largest K: the sampled
+    rows bit-exact against the oracle's dequantized weights, every value
+    finite."""
+    print("[case] dequant at the limits", N, K, fmt, flush=True)
+    wq, sq, codes, scales, cols = _weights_with_sampled_tiles(N, K, fmt, 2000 + fmt)
+    W = F.dequant(wq, sq, N, K, fmt)
+    torch.cuda.synchronize()
+    del wq, sq
+    assert bool(torch.isfinite(W).all())
+    got = _bits(W.index_select(0, torch.from_numpy(cols).cuda()))
+    del W
+    torch.cuda.empty_cache()
+    want = oracle.bf16_bits_of_exact(oracle.dequant_weights(codes, scales, K, fmt))
+    nz = oracle.dequant_weights(codes, scales, K, fmt) != 0
+    assert np.array_equal(got[nz], want[nz]), np.argwhere((got != want) & nz)[:5]
+    assert not np.any(oracle.bf16_bits_to_f64(got)[~nz]), "zero weights dequantize to +-0"

@@ -250,9 +250,12 @@ def dequant(wq, sq, N: int, K: int, fmt: int, out=None, stream=None, dtype=None)
     dtype = torch.bfloat16 if dtype is None else dtype
     if dtype not in (torch.bfloat16, torch.float16):
         raise ValueError("dtype must be torch.bfloat16 or torch.float16")
+    for t in (wq, sq):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("wq / sq must be contiguous uint8 CUDA tensors")
     nw, ns = repack_size(N, K, fmt)
-    if wq.numel() != nw or sq.numel() != ns or not wq.is_cuda or not sq.is_cuda:
-        raise ValueError("packed weight tensors have the wrong size or device")
+    if wq.numel() != nw or sq.numel() != ns:
+        raise ValueError("packed weight tensors have the wrong size")
     if out is None:
         out = torch.empty((N, K), dtype=dtype, device=wq.device)
     elif out.shape != (N, K) or out.dtype != dtype or not out.is_cuda or not out.is_contiguous():

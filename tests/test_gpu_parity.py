@@ -414,6 +414,14 @@ def test_binding_rejects_tensors_off_the_device():
         F.gemm(A, wq.cpu(), sq, p.N, p.K, p.fmt)
     with pytest.raises(ValueError):
         F.dequant(wq, sq.cpu(), p.N, p.K, p.fmt)
+    # one byte expanded to the packed size (stride 0: the kernel would read
+    # past its allocation) and the right element count in the wrong type
+    with pytest.raises(ValueError):
+        F.dequant(wq[:1].expand(wq.numel()), sq, p.N, p.K, p.fmt)
+    with pytest.raises(ValueError):
+        F.dequant(wq, torch.zeros(sq.numel(), dtype=torch.float32, device="cuda"), p.N, p.K, p.fmt)
+    with pytest.raises(ValueError):
+        F.gemm(A, wq[:1].expand(wq.numel()), sq, p.N, p.K, p.fmt)
     torch.cuda.synchronize()
     y = F.gemm(A, wq, sq, p.N, p.K, p.fmt)  # the valid call still works
     torch.cuda.synchronize()
